@@ -1,0 +1,221 @@
+"""Benchmark of the APB per-host prefill path on one MI355X.
+
+One step = one host's share of one layer: score (apb_score_kv), top-l + gather
+(apb_topk_gather), passing block (apb_build_passing) and attention
+(apb_block_attention), on synthetic inputs already resident in HBM.  The
+compressed blocks of the earlier hosts are produced before timing, in place of
+the all-gather between hosts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
+
+Prints one JSON line.  `value` is prefill tokens/s of the host block (L / step
+time); `roofline` covers the attention kernel (HIP events around its launches);
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s + prefill tokens/s per host block; % bf16 MFMA peak"
+# MI355X dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP/CU/clock (the published 2.5 PFLOP/s).
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_attention_llama8b_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "sparse_block_attention_amd", "csrc", "block_attention.hip")
+
+DESCRIPTIONS = {
+    "llama8b": "Llama-3.1-8B-shaped layer, last of 8 hosts at 128K (L=16384, A=2048, P=7x1024)",
+    "qwen14b": "Qwen-2.5-14B-shaped layer, last of 8 hosts at 128K (L=16384, A=4096, P=7x2048)",
+    "yi34b": "Yi-34B-200K-shaped layer, last of 8 hosts at 200K (L=25600, A=3200, P=7x1600)",
+    "llama1m": "Llama-3-8B-1M-shaped layer, last of 8 hosts at 1M (L=131072, A=16384, P=7x4096)",
+    "tiny": "tiny: 1024 tokens over 4 hosts of 256, anchor 64, l=32",
+}
+
+
+def attention_flops(w) -> float:
+    """Algorithmic FLOPs of the attention: QK^T and PV over the visible pairs only."""
+    L, A, P = w.local_len, w.anchor_len, w.pass_len
+    pairs = L * A + L * P + L * (L + 1) // 2
+    return 4.0 * w.head_dim * w.n_q_heads * pairs
+
+
+def attention_bytes(w) -> float:
+    """Algorithmic HBM bytes of one attention launch: q, anchor/passing/local K and V read once,
+    O and LSE written once."""
+    d, Hq, Hkv = w.head_dim, w.n_q_heads, w.n_kv_heads
+    L, A, P = w.local_len, w.anchor_len, w.pass_len
+    return 2.0 * L * Hq * d * 2 + 2.0 * (A + P + L) * Hkv * d * 2 + 4.0 * Hq * L
+
+
+def _src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs, or None when
+    absent, for another workload, or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("kernel_source_sha256") != _src_hash(ATTN_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, blocks, weights, anchor, n_rows=128):
+    """Time the CPU oracle on a bounded sample of one host step; scale to tokens/s."""
+    from oracle import apb_oracle as orc
+    from sparse_block_attention_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()
+                     if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = os.cpu_count() or 1
+    q, k, v = blocks
+    L = w.local_len
+    t0 = time.perf_counter()
+    s = orc.score_kv(q, k, v, weights["w1"], weights["b1"], weights["w2"], weights["b2"])
+    t1 = time.perf_counter()
+    idx = orc.topl(s, w.pass_per_host)
+    orc.gather(k, v, idx)
+    t2 = time.perf_counter()
+    comps = [(synth.random_bf16((w.pass_per_host, w.n_kv_heads, w.head_dim), 90, stream=j),
+              synth.random_bf16((w.pass_per_host, w.n_kv_heads, w.head_dim), 91, stream=j))
+             for j in range(w.host)]
+    t2b = time.perf_counter()
+    kp, vp = orc.build_passing([c[0] for c in comps], [c[1] for c in comps])
+    t3 = time.perf_counter()
+    rows = np.linspace(0, L - 1, n_rows).round().astype(np.int64)
+    orc.block_attention(q, anchor[0], anchor[1], kp, vp, k, v, rows=rows)
+    t4 = time.perf_counter()
+    pre = w.anchor_len + w.pass_len
+    all_pairs = L * pre + L * (L + 1) // 2
+    sample_pairs = int((pre + rows + 1).sum())
+    t_attn = (t4 - t3) * all_pairs / sample_pairs
+    t_total = (t1 - t0) + (t2 - t1) + (t3 - t2b) + t_attn
+    return {
+        "value": L / t_total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+        "sample": (f"scoring, top-l and gather over the whole {L}-token block; passing build of "
+                   f"{w.host} blocks; attention for {n_rows} evenly spaced query rows x "
+                   f"{w.n_q_heads} heads ({sample_pairs} of {all_pairs} visible pairs per head, "
+                   f"scaled by the pair count); float64 numpy"),
+        "seconds_measured": round(t4 - t0, 2), "seconds_extrapolated": round(t_total, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the per-host path has no collective in this build "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_block_attention_amd import binding as B
+    from sparse_block_attention_amd import pipeline, synth
+    from sparse_block_attention_amd.tensors import to_device_bf16, to_device_f32
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.lib()
+    w = synth.WORKLOADS[args.workload]
+    pr = B.Problem(w.n_q_heads, w.n_kv_heads, w.head_dim, w.local_len, w.anchor_len,
+                   w.pass_per_host, w.host, w.n_hosts, None)
+    print(f"# generating {w.name} inputs", file=sys.stderr, flush=True)
+    wts = synth.scorer_weights(w)
+    sc = {"w1": to_device_bf16(wts["w1"]), "b1": to_device_f32(wts["b1"]),
+          "w2": to_device_f32(wts["w2"]), "b2": to_device_f32(wts["b2"])}
+    ka_np, va_np = synth.anchor_kv(w)
+    ka = to_device_bf16(ka_np) if w.anchor_len else None
+    va = to_device_bf16(va_np) if w.anchor_len else None
+    kcs, vcs = [], []
+    host_np = None
+    for j in range(w.host + 1):
+        q, k, v = synth.host_block(w, j)
+        ht = pipeline.HostTensors(to_device_bf16(q), to_device_bf16(k), to_device_bf16(v))
+        if j < w.host:
+            pj = B.Problem(w.n_q_heads, w.n_kv_heads, w.head_dim, w.local_len, w.anchor_len,
+                           w.pass_per_host, j, w.n_hosts, None)
+            _, _, kc, vc = pipeline.compress(pj, sc, ht)
+            kcs.append(kc)
+            vcs.append(vc)
+            del ht
+        else:
+            host = ht
+            host_np = (q, k, v)
+    torch.cuda.synchronize()
+    buf = pipeline.StepBuffers.allocate(pr)
+    stream = torch.cuda.current_stream()
+    print("# warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        pipeline.host_step(pr, sc, host, ka, va, kcs, vcs, buf, stream=stream)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    print("# timed steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        pipeline.host_step(pr, sc, host, ka, va, kcs, vcs, buf, stream=stream, attn_events=ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = attention_flops(w)
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    traffic = measured_traffic(w.name)
+
+    result = {
+        "metric": METRIC,
+        "value": w.local_len / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {DESCRIPTIONS[w.name]}", "local_len": w.local_len,
+                   "anchor_len": w.anchor_len, "pass_len": w.pass_len, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "scorer_hidden": w.hidden,
+                   "host_index": w.host, "n_hosts": w.n_hosts},
+        "attention": {"ms": attn_ms, "tflops": achieved, "frac_bf16_peak": achieved / PEAK_BF16_TFLOPS,
+                      "tflop_per_launch": flops / 1e12},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
+    }
+    del buf, host, kcs, vcs
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle on a bounded sample)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, host_np, wts, (ka_np, va_np))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * apb.h - C ABI of the APB per-host prefill path on AMD MI355X (gfx950).
+ *
+ * APB ("Accelerating Distributed Long-Context Inference by Passing Compressed
+ * Context Blocks across GPUs") splits a long prompt evenly over hosts.  One
+ * host's share of one layer is four steps, each an entry point below:
+ *
+ *   apb_score_kv         score every local token per kv head (stand-in for
+ *                        Locret's retaining heads);
+ *   apb_topk_gather      keep the l best tokens per kv head and gather their
+ *                        K/V rows: the host's compressed context block;
+ *   apb_build_passing    concatenate the compressed blocks of the preceding
+ *                        hosts: the passing block;
+ *   apb_block_attention  attention of the local queries over
+ *                        [anchor | passing | local, causal].
+ *
+ * The steps are described on the juejin.cn explainer of APB, sections
+ * "APB 的主要功能" (main functions) and "APB 的技术原理" (technical principles),
+ * and in the paper's arXiv abstract (mlsanity.com/paper/2502.12085).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are caller-owned, contiguous, row-major DEVICE buffers, token
+ *     major: [rows][heads][head_dim].  bf16 tensors are passed as void*.
+ *     Every tensor pointer must be 16-byte aligned.  Outputs must not alias
+ *     inputs.  The library allocates no device memory and keeps no state
+ *     between calls other than a per-process cache of device properties.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are asynchronous on that stream, reentrant and deterministic
+ *     (identical inputs give identical output bits; no result depends on the
+ *     order of atomic operations).
+ *   - Arguments are checked on the host before anything is launched; a bad
+ *     argument returns an error code and launches nothing.  A launch failure
+ *     returns APB_ERR_HIP.  Faults inside a kernel surface at the caller's
+ *     next synchronisation, as in HIP.  No call aborts, exits or throws;
+ *     apb_last_error() gives a message for the calling thread's last error.
+ */
+#ifndef APB_H
+#define APB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define APB_ABI_VERSION 1
+
+/* Upper limits of this implementation (APB_ERR_UNSUPPORTED beyond them). */
+#define APB_MAX_Q_HEADS 256
+#define APB_MAX_LOCAL_LEN (1 << 26)
+#define APB_MAX_PASS_HOSTS_PER_LAUNCH 128
+
+typedef enum {
+  APB_OK = 0,
+  APB_ERR_INVALID_ARGUMENT = 1, /* NULL / misaligned pointer, inconsistent sizes */
+  APB_ERR_UNSUPPORTED = 2,      /* valid in principle, outside this build's limits */
+  APB_ERR_HIP = 3,              /* the HIP runtime reported an error */
+  APB_ERR_INTERNAL = 4
+} apb_status;
+
+/*
+ * One host's share of the split sequence (explainer, "APB 的主要功能": the
+ * input is distributed evenly over hosts, an anchor block holding the start of
+ * the sequence is prepended to each local block, and the passing block carries
+ * the important KV of the preceding hosts).  Host memory, read during the call.
+ */
+typedef struct {
+  int32_t n_q_heads;       /* Hq, 1..APB_MAX_Q_HEADS, a multiple of n_kv_heads       */
+  int32_t n_kv_heads;      /* Hkv >= 1; g = Hq / Hkv q heads share one kv head      */
+  int32_t head_dim;        /* d: 64 or 128                                           */
+  int32_t local_len;       /* L: tokens in this host's block, 1..APB_MAX_LOCAL_LEN  */
+  int32_t anchor_len;      /* A >= 0: anchor rows (the first A tokens of the sequence) */
+  int32_t pass_per_host;   /* l: tokens kept per kv head per host, 0 <= l <= L       */
+  int32_t host_index;      /* p: this host, 0 <= p < n_hosts; passing has P = p*l rows */
+  int32_t n_hosts;         /* H >= 1                                                  */
+  const int32_t *kv_head_of_q; /* host array [Hq] mapping q head -> kv head, or NULL
+                                  for i -> i / g.  Each kv head must get exactly g q
+                                  heads; a kv head's group is taken in ascending
+                                  q-head order.                                      */
+} apb_problem;
+
+/*
+ * Per-kv-head 2-layer scorer standing in for Locret's retaining heads
+ * (explainer, "APB 的主要功能": each host compresses its KV cache with retaining
+ * heads; "APB 的技术原理": the query sits at the start of the anchor so the
+ * compressor sees it).  For kv head h and token t:
+ *     x = [q[t, G_h[0]]; ...; q[t, G_h[g-1]]; k[t, h]; v[t, h]]   ((g+2)*d values)
+ *     s = w2[h] . relu(W1[h] x + b1[h]) + b2[h]
+ * Device pointers.  Products of bf16 values are accumulated in fp32.
+ */
+typedef struct {
+  int32_t hidden;          /* Hs: a multiple of 32, 32..256                    */
+  const void *w1;          /* bf16 [Hkv][Hs][(g+2)*d]  (nn.Linear weight layout) */
+  const float *b1;         /* fp32 [Hkv][Hs]                                    */
+  const float *w2;         /* fp32 [Hkv][Hs]                                    */
+  const float *b2;         /* fp32 [Hkv]                                        */
+} apb_scorer;
+
+/*
+ * Step 1: importance score of every local token, per kv head.
+ *   q_local  bf16 [L][Hq][d]      k_local, v_local  bf16 [L][Hkv][d]
+ *   scores   fp32 [Hkv][L]        (output)
+ */
+apb_status apb_score_kv(const apb_problem *problem, const apb_scorer *scorer,
+                        const void *q_local, const void *k_local, const void *v_local,
+                        float *scores, void *stream);
+
+/*
+ * Step 2: per kv head, keep the l highest scores and gather their K/V rows
+ * into the compressed context block (explainer, "APB 的主要功能", compression
+ * with retaining heads and the communication of the compressed blocks).
+ * Order: larger fp32 score first; -0 equals +0; NaN ranks below every number
+ * (including -inf); equal scores go to the lower token index.
+ *   scores          fp32 [Hkv][L]
+ *   k_local, v_local bf16 [L][Hkv][d]
+ *   idx             int32 [Hkv][l] (output) selected local token indices, ascending
+ *   k_comp, v_comp  bf16 [l][Hkv][d] (output) k_comp[s][h] = k_local[idx[h][s]][h]
+ * With l == 0 nothing is written and the pointers may be NULL.
+ */
+apb_status apb_topk_gather(const apb_problem *problem, const float *scores,
+                           const void *k_local, const void *v_local,
+                           int32_t *idx, void *k_comp, void *v_comp, void *stream);
+
+/*
+ * Step 3: passing block from the compressed blocks of hosts 0..p-1 (explainer,
+ * "APB 的主要功能": the all-gathered compressed blocks form the passing block of
+ * the preceding hosts' important KV; "APB 的技术原理": each block is compressed
+ * and sent to the later GPUs).  Host-major: row j*l + s holds slot s of host j.
+ *   k_comp_hosts, v_comp_hosts  HOST arrays of p device pointers, each bf16 [l][Hkv][d]
+ *   k_pass, v_pass              bf16 [p*l][Hkv][d] (output)
+ * With P == 0 nothing is written and every pointer may be NULL.
+ */
+apb_status apb_build_passing(const apb_problem *problem,
+                             const void *const *k_comp_hosts, const void *const *v_comp_hosts,
+                             void *k_pass, void *v_pass, void *stream);
+
+/*
+ * Step 4: attention of the local queries (explainer, "APB 的主要功能": each host
+ * attends over the anchor block, the passing block and its local block; the
+ * passing block is dropped afterwards).  Local query row r of q head i
+ * (kv head h = map[i]) sees every anchor row, every passing row and local rows
+ * 0..r of kv head h:
+ *     O[r][i] = softmax(scale * q[r][i] . K^T) V,   lse[i][r] = ln(sum exp(...))
+ *   q_local            bf16 [L][Hq][d]
+ *   k_anchor, v_anchor bf16 [A][Hkv][d]  (may be NULL iff A == 0)
+ *   k_pass, v_pass     bf16 [P][Hkv][d]  (may be NULL iff P == 0), P = p * l
+ *   k_local, v_local   bf16 [L][Hkv][d]
+ *   softmax_scale      finite, > 0 (commonly 1/sqrt(d))
+ *   out                bf16 [L][Hq][d] (output, rounded to nearest even)
+ *   lse                fp32 [Hq][L]    (output, natural log) or NULL
+ * bf16 products, fp32 accumulation and fp32 online softmax.
+ */
+apb_status apb_block_attention(const apb_problem *problem, const void *q_local,
+                               const void *k_anchor, const void *v_anchor,
+                               const void *k_pass, const void *v_pass,
+                               const void *k_local, const void *v_local,
+                               float softmax_scale, void *out, float *lse, void *stream);
+
+/* Host-only checks of a problem description; launches nothing. */
+apb_status apb_validate_problem(const apb_problem *problem);
+
+/* Static text for a status code. */
+const char *apb_status_string(apb_status status);
+
+/* Message describing the calling thread's most recent error ("" if none). */
+const char *apb_last_error(void);
+
+/* APB_ABI_VERSION of the loaded library. */
+int apb_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* APB_H */

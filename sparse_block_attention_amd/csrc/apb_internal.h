@@ -1,0 +1,60 @@
+// Internal declarations shared by the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace apb {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Number of XCDs on MI355X; workgroups are dispatched to them round-robin.
+constexpr int kNumXcd = 8;
+
+// Attention over [anchor | passing | local causal].
+struct AttnArgs {
+  const uint16_t *q, *ka, *va, *kp, *vp, *kl, *vl;
+  uint16_t *out;
+  float *lse;               // may be null
+  int L, A, P, Hq, Hkv, g;
+  int n_qtiles;             // ceil(L / rows per workgroup)
+  int n_work;               // n_qtiles * Hq
+  float scale_log2;         // softmax scale * log2(e)
+  uint8_t qhead_of_slot[256];  // slot h*g + j -> j-th q head (ascending) of kv head h
+};
+hipError_t launch_block_attention(AttnArgs &a, int head_dim, hipStream_t s);
+
+// Scorer: per kv head, 2-layer ReLU MLP over [q of the group; k; v].
+struct ScoreArgs {
+  const uint16_t *q, *k, *v, *w1;
+  const float *b1, *w2, *b2;
+  float *scores;
+  int L, Hq, Hkv, g, d, hidden;
+  int n_ttiles;             // ceil(L / tokens per workgroup)
+  uint8_t qhead_of_slot[256];
+};
+hipError_t launch_score_kv(ScoreArgs &a, hipStream_t s);
+
+// Top-l selection + gather.
+struct TopkArgs {
+  const float *scores;
+  const uint16_t *k, *v;
+  int32_t *idx;
+  uint16_t *kc, *vc;
+  int L, l, Hkv, d;
+};
+hipError_t launch_topk_gather(const TopkArgs &a, hipStream_t s);
+
+// Passing-block assembly: up to 128 source blocks per launch.
+struct PassArgs {
+  const uint16_t *ksrc[128];
+  const uint16_t *vsrc[128];
+  uint16_t *kdst, *vdst;
+  long long block_u16x8;    // 16-byte units per compressed block (l * Hkv * d / 8)
+  int n_src;
+};
+hipError_t launch_build_passing(const PassArgs &a, hipStream_t s);
+
+}  // namespace apb

@@ -1,0 +1,199 @@
+// C-ABI entry points: check arguments on the host, then launch the HIP kernels
+// on the caller's stream.  Nothing is allocated; no exception crosses the ABI.
+#include <math.h>
+#include <string.h>
+
+#include "apb_host.h"
+#include "apb_internal.h"
+
+using apb_host::aligned16;
+using apb_host::fail;
+
+namespace {
+
+apb_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return APB_OK;
+  return fail(APB_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+apb_status need_ptr(const void *p, const char *name) {
+  if (p == nullptr) return fail(APB_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned16(p)) return fail(APB_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return APB_OK;
+}
+
+#define APB_TRY(expr)              \
+  do {                             \
+    apb_status st_ = (expr);       \
+    if (st_ != APB_OK) return st_; \
+  } while (0)
+
+apb_status score_kv(const apb_problem *pr, const apb_scorer *sc, const void *q, const void *k, const void *v,
+                    float *scores, void *stream) {
+  APB_TRY(apb_host::check_problem(pr));
+  if (sc == nullptr) return fail(APB_ERR_INVALID_ARGUMENT, "scorer is NULL");
+  if (sc->hidden < 32 || sc->hidden > 256 || sc->hidden % 32 != 0)
+    return fail(APB_ERR_UNSUPPORTED, "scorer hidden = %d, supported: multiples of 32 in [32, 256]", sc->hidden);
+  APB_TRY(need_ptr(sc->w1, "scorer.w1"));
+  APB_TRY(need_ptr(sc->b1, "scorer.b1"));
+  APB_TRY(need_ptr(sc->w2, "scorer.w2"));
+  APB_TRY(need_ptr(sc->b2, "scorer.b2"));
+  APB_TRY(need_ptr(q, "q_local"));
+  APB_TRY(need_ptr(k, "k_local"));
+  APB_TRY(need_ptr(v, "v_local"));
+  APB_TRY(need_ptr(scores, "scores"));
+  apb::ScoreArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = static_cast<const uint16_t *>(q);
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.w1 = static_cast<const uint16_t *>(sc->w1);
+  a.b1 = sc->b1;
+  a.w2 = sc->w2;
+  a.b2 = sc->b2;
+  a.scores = scores;
+  a.L = pr->local_len;
+  a.Hq = pr->n_q_heads;
+  a.Hkv = pr->n_kv_heads;
+  a.g = pr->n_q_heads / pr->n_kv_heads;
+  a.d = pr->head_dim;
+  a.hidden = sc->hidden;
+  apb_host::slot_table(pr, a.qhead_of_slot);
+  return hip_status(apb::launch_score_kv(a, static_cast<hipStream_t>(stream)), "apb_score_kv launch");
+}
+
+apb_status topk_gather(const apb_problem *pr, const float *scores, const void *k, const void *v, int32_t *idx,
+                       void *kc, void *vc, void *stream) {
+  APB_TRY(apb_host::check_problem(pr));
+  if (pr->pass_per_host == 0) return APB_OK;
+  APB_TRY(need_ptr(scores, "scores"));
+  APB_TRY(need_ptr(k, "k_local"));
+  APB_TRY(need_ptr(v, "v_local"));
+  APB_TRY(need_ptr(idx, "idx"));
+  APB_TRY(need_ptr(kc, "k_comp"));
+  APB_TRY(need_ptr(vc, "v_comp"));
+  apb::TopkArgs a;
+  a.scores = scores;
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.idx = idx;
+  a.kc = static_cast<uint16_t *>(kc);
+  a.vc = static_cast<uint16_t *>(vc);
+  a.L = pr->local_len;
+  a.l = pr->pass_per_host;
+  a.Hkv = pr->n_kv_heads;
+  a.d = pr->head_dim;
+  return hip_status(apb::launch_topk_gather(a, static_cast<hipStream_t>(stream)), "apb_topk_gather launch");
+}
+
+apb_status build_passing(const apb_problem *pr, const void *const *kh, const void *const *vh, void *kp, void *vp,
+                         void *stream) {
+  APB_TRY(apb_host::check_problem(pr));
+  const int p = pr->host_index;
+  const long long l = pr->pass_per_host;
+  if (p == 0 || l == 0) return APB_OK;
+  if (kh == nullptr || vh == nullptr) return fail(APB_ERR_INVALID_ARGUMENT, "host pointer arrays are NULL");
+  APB_TRY(need_ptr(kp, "k_pass"));
+  APB_TRY(need_ptr(vp, "v_pass"));
+  for (int j = 0; j < p; ++j) {
+    if (kh[j] == nullptr || !aligned16(kh[j]))
+      return fail(APB_ERR_INVALID_ARGUMENT, "k_comp_hosts[%d] is NULL or not 16-byte aligned", j);
+    if (vh[j] == nullptr || !aligned16(vh[j]))
+      return fail(APB_ERR_INVALID_ARGUMENT, "v_comp_hosts[%d] is NULL or not 16-byte aligned", j);
+  }
+  const long long units = l * pr->n_kv_heads * pr->head_dim / 8;  // 16-byte units per block
+  for (int j0 = 0; j0 < p; j0 += APB_MAX_PASS_HOSTS_PER_LAUNCH) {
+    apb::PassArgs a;
+    memset(&a, 0, sizeof a);
+    const int n = (p - j0 < APB_MAX_PASS_HOSTS_PER_LAUNCH) ? p - j0 : APB_MAX_PASS_HOSTS_PER_LAUNCH;
+    for (int j = 0; j < n; ++j) {
+      a.ksrc[j] = static_cast<const uint16_t *>(kh[j0 + j]);
+      a.vsrc[j] = static_cast<const uint16_t *>(vh[j0 + j]);
+    }
+    a.kdst = static_cast<uint16_t *>(kp) + (long long)j0 * units * 8;
+    a.vdst = static_cast<uint16_t *>(vp) + (long long)j0 * units * 8;
+    a.block_u16x8 = units;
+    a.n_src = n;
+    APB_TRY(hip_status(apb::launch_build_passing(a, static_cast<hipStream_t>(stream)), "apb_build_passing launch"));
+  }
+  return APB_OK;
+}
+
+apb_status block_attention(const apb_problem *pr, const void *q, const void *ka, const void *va, const void *kp,
+                           const void *vp, const void *kl, const void *vl, float scale, void *out, float *lse,
+                           void *stream) {
+  APB_TRY(apb_host::check_problem(pr));
+  const long long P = (long long)pr->host_index * pr->pass_per_host;
+  APB_TRY(need_ptr(q, "q_local"));
+  APB_TRY(need_ptr(kl, "k_local"));
+  APB_TRY(need_ptr(vl, "v_local"));
+  APB_TRY(need_ptr(out, "out"));
+  if (pr->anchor_len > 0) {
+    APB_TRY(need_ptr(ka, "k_anchor"));
+    APB_TRY(need_ptr(va, "v_anchor"));
+  }
+  if (P > 0) {
+    APB_TRY(need_ptr(kp, "k_pass"));
+    APB_TRY(need_ptr(vp, "v_pass"));
+  }
+  if (lse != nullptr && !aligned16(lse)) return fail(APB_ERR_INVALID_ARGUMENT, "lse is not 16-byte aligned");
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(APB_ERR_INVALID_ARGUMENT, "softmax_scale = %g, need finite and > 0", (double)scale);
+  apb::AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = static_cast<const uint16_t *>(q);
+  a.ka = static_cast<const uint16_t *>(ka);
+  a.va = static_cast<const uint16_t *>(va);
+  a.kp = static_cast<const uint16_t *>(kp);
+  a.vp = static_cast<const uint16_t *>(vp);
+  a.kl = static_cast<const uint16_t *>(kl);
+  a.vl = static_cast<const uint16_t *>(vl);
+  a.out = static_cast<uint16_t *>(out);
+  a.lse = lse;
+  a.L = pr->local_len;
+  a.A = pr->anchor_len;
+  a.P = (int)P;
+  a.Hq = pr->n_q_heads;
+  a.Hkv = pr->n_kv_heads;
+  a.g = pr->n_q_heads / pr->n_kv_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  apb_host::slot_table(pr, a.qhead_of_slot);
+  return hip_status(apb::launch_block_attention(a, pr->head_dim, static_cast<hipStream_t>(stream)),
+                    "apb_block_attention launch");
+}
+
+}  // namespace
+
+#define APB_GUARD(call)                                                 \
+  try {                                                                 \
+    apb_host::clear_error();                                            \
+    return call;                                                        \
+  } catch (...) {                                                       \
+    return fail(APB_ERR_INTERNAL, "unexpected C++ exception in %s", __func__); \
+  }
+
+extern "C" {
+
+apb_status apb_score_kv(const apb_problem *problem, const apb_scorer *scorer, const void *q_local,
+                        const void *k_local, const void *v_local, float *scores, void *stream) {
+  APB_GUARD(score_kv(problem, scorer, q_local, k_local, v_local, scores, stream));
+}
+
+apb_status apb_topk_gather(const apb_problem *problem, const float *scores, const void *k_local,
+                           const void *v_local, int32_t *idx, void *k_comp, void *v_comp, void *stream) {
+  APB_GUARD(topk_gather(problem, scores, k_local, v_local, idx, k_comp, v_comp, stream));
+}
+
+apb_status apb_build_passing(const apb_problem *problem, const void *const *k_comp_hosts,
+                             const void *const *v_comp_hosts, void *k_pass, void *v_pass, void *stream) {
+  APB_GUARD(build_passing(problem, k_comp_hosts, v_comp_hosts, k_pass, v_pass, stream));
+}
+
+apb_status apb_block_attention(const apb_problem *problem, const void *q_local, const void *k_anchor,
+                               const void *v_anchor, const void *k_pass, const void *v_pass, const void *k_local,
+                               const void *v_local, float softmax_scale, void *out, float *lse, void *stream) {
+  APB_GUARD(block_attention(problem, q_local, k_anchor, v_anchor, k_pass, v_pass, k_local, v_local, softmax_scale,
+                            out, lse, stream));
+}
+
+}  // extern "C"

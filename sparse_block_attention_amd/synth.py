@@ -182,3 +182,9 @@ def tie_heavy_scores(n_heads: int, n: int, seed: int, specials: bool = True) -> 
 def default_head_map(n_q_heads: int, n_kv_heads: int) -> np.ndarray:
     g = n_q_heads // n_kv_heads
     return (np.arange(n_q_heads) // g).astype(np.int32)
+
+
+def random_bf16(shape, seed: int, sigma: float = 1.0, stream: int = 0) -> np.ndarray:
+    """Seeded N(0, sigma^2) draws rounded to bf16 (float32 array), for arbitrary shapes."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(77, stream))))
+    return _normal_bf16(rng, shape, sigma)

@@ -1,0 +1,199 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every stage is fed the GPU's own output of the previous stage, so a near-tie
+in one score cannot cascade: top-l is checked bit-exact against the oracle run
+on the GPU's fp32 scores, gather and passing bit-exact against the oracle fed
+the GPU's indices.  Bars are in apb_gpu_util.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import apb_oracle as orc
+from sparse_block_attention_amd import binding as B
+from sparse_block_attention_amd import pipeline, synth
+from sparse_block_attention_amd.tensors import from_device_bf16, to_device_bf16, to_device_f32
+
+from apb_gpu_util import check_attention, check_scores, require_gpu, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _problem(w: synth.Workload, host=None, head_map=None) -> B.Problem:
+    return B.Problem(w.n_q_heads, w.n_kv_heads, w.head_dim, w.local_len, w.anchor_len,
+                     w.pass_per_host, w.host if host is None else host, w.n_hosts, head_map)
+
+
+def _dev_scorer(wts):
+    return {"w1": to_device_bf16(wts["w1"]), "b1": to_device_f32(wts["b1"]),
+            "w2": to_device_f32(wts["w2"]), "b2": to_device_f32(wts["b2"])}
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _run_workload(w: synth.Workload, check_hosts, rows=None, score_rows=None, head_map=None):
+    """Run every host's compression and the evaluated host's attention; check stages."""
+    wts = synth.scorer_weights(w)
+    sc = _dev_scorer(wts)
+    ka_np, va_np = synth.anchor_kv(w)
+    kcs, vcs, kc_np, vc_np = [], [], [], []
+    for j in range(w.host + 1):
+        q, k, v = synth.host_block(w, j)
+        pr = _problem(w, j, head_map)
+        host = pipeline.HostTensors(to_device_bf16(q), to_device_bf16(k), to_device_bf16(v))
+        scores, idx, kc, vc = pipeline.compress(pr, sc, host)
+        torch.cuda.synchronize()
+        s_np, idx_np = _np(scores), _np(idx)
+        if j in check_hosts:
+            tr = np.arange(w.local_len) if score_rows is None else score_rows
+            s_ref = orc.score_kv(q[tr], k[tr], v[tr], wts["w1"], wts["b1"], wts["w2"], wts["b2"],
+                                 kv_head_of_q=head_map)
+            check_scores(s_np[:, tr], s_ref, f"host {j} scores")
+            assert np.array_equal(idx_np, orc.topl(s_np, w.pass_per_host)), f"host {j} top-l"
+            kr, vr = orc.gather(k, v, idx_np)
+            assert np.array_equal(from_device_bf16(kc), kr), f"host {j} k_comp"
+            assert np.array_equal(from_device_bf16(vc), vr), f"host {j} v_comp"
+        if j < w.host:
+            kcs.append(kc)
+            vcs.append(vc)
+            kc_np.append(from_device_bf16(kc))
+            vc_np.append(from_device_bf16(vc))
+        else:
+            pr = _problem(w, j, head_map)
+            kp, vp = (B.apb_build_passing(pr, kcs, vcs) if pr.pass_len else (None, None))
+            kp_np = vp_np = None
+            if pr.pass_len:
+                kp_ref, vp_ref = orc.build_passing(kc_np, vc_np)
+                kp_np, vp_np = from_device_bf16(kp), from_device_bf16(vp)
+                assert np.array_equal(kp_np, kp_ref) and np.array_equal(vp_np, vp_ref), "passing"
+            out, lse = B.apb_block_attention(pr, host.q, to_device_bf16(ka_np) if w.anchor_len else None,
+                                             to_device_bf16(va_np) if w.anchor_len else None, kp, vp,
+                                             host.k, host.v)
+            torch.cuda.synchronize()
+            o_np = from_device_bf16(out)
+            lse_np = _np(lse)
+            rr = np.arange(w.local_len) if rows is None else rows
+            o_ref, lse_ref = orc.block_attention(q, ka_np, va_np, kp_np, vp_np, k, v,
+                                                 kv_head_of_q=head_map, rows=rr)
+            return check_attention(o_np[rr], o_ref, lse_np[:, rr], lse_ref, f"{w.name} attention")
+
+
+def test_tiny_workload_all_rows():
+    """1024 tokens over 4 hosts, every stage, every row and head."""
+    _run_workload(synth.WORKLOADS["tiny"], check_hosts=range(4))
+
+
+def test_llama8b_full_size_sampled_rows():
+    """Llama-3.1-8B layer, last of 8 hosts at 128K, in the benchmark's launch configuration.
+
+    Scores on sampled tokens, top-l / gather / passing in full, attention on sampled rows of
+    every q head.
+    """
+    w = synth.WORKLOADS["llama8b"]
+    rows = sample_rows(w.local_len, 40, seed=1)
+    score_rows = sample_rows(w.local_len, 300, seed=2)
+    _run_workload(w, check_hosts={0, w.host}, rows=rows, score_rows=score_rows)
+
+
+@pytest.mark.parametrize("cfg", [
+    # name, config id, hosts, L, A, l, Hq, Hkv, d, Hs, head map
+    ("ragged", 201, 4, 200, 70, 33, 4, 2, 128, 64, None),
+    ("g5_no_anchor", 202, 2, 300, 0, 33, 5, 1, 128, 96, None),
+    ("g7_no_passing", 203, 3, 129, 17, 0, 7, 1, 64, 32, None),
+    ("custom_map", 204, 3, 257, 64, 32, 6, 3, 128, 256, [2, 0, 1, 1, 0, 2]),
+    ("d64_multi_tile", 205, 5, 512, 128, 64, 8, 2, 64, 128, None),
+    ("single_token", 206, 1, 1, 0, 1, 2, 1, 64, 32, None),
+    ("l_equals_L", 207, 3, 96, 8, 96, 2, 1, 128, 32, None),
+])
+def test_small_workloads_all_rows(cfg):
+    name, cid, H, L, A, l, Hq, Hkv, d, Hs, hm = cfg
+    w = synth.Workload(name, cid, H, L, A, l, Hq, Hkv, d, Hs, 1.0, min(2, H * L))
+    _run_workload(w, check_hosts=range(H), head_map=hm)
+
+
+@pytest.mark.parametrize("L,A,p,l,Hq,Hkv,d", [
+    (1, 0, 0, 0, 2, 1, 128),
+    (64, 0, 0, 0, 2, 1, 128),
+    (65, 1, 1, 1, 3, 3, 64),
+    (700, 300, 0, 0, 4, 1, 128),
+    (130, 0, 5, 100, 2, 2, 128),
+])
+def test_attention_segment_edges(L, A, p, l, Hq, Hkv, d):
+    """Empty, single-row and non-multiple-of-tile segments, random inputs."""
+    P = p * l
+    q = synth.random_bf16((L, Hq, d), 1, stream=L)
+    ka, va = synth.random_bf16((A, Hkv, d), 2, stream=L), synth.random_bf16((A, Hkv, d), 3, stream=L)
+    kp, vp = synth.random_bf16((P, Hkv, d), 4, stream=L), synth.random_bf16((P, Hkv, d), 5, stream=L)
+    kl, vl = synth.random_bf16((L, Hkv, d), 6, stream=L), synth.random_bf16((L, Hkv, d), 7, stream=L)
+    pr = B.Problem(Hq, Hkv, d, L, A, l, p, p + 1, None)
+    dv = lambda x, n: to_device_bf16(x) if n else None
+    out, lse = B.apb_block_attention(pr, to_device_bf16(q), dv(ka, A), dv(va, A), dv(kp, P), dv(vp, P),
+                                     to_device_bf16(kl), to_device_bf16(vl), softmax_scale=0.1)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.block_attention(q, ka, va, kp, vp, kl, vl, scale=0.1)
+    check_attention(from_device_bf16(out), o_ref, _np(lse), lse_ref, "segment edges")
+
+
+@pytest.mark.parametrize("L,l,specials", [
+    (1, 1, True), (7, 3, True), (256, 85, True), (16384, 1024, True), (16385, 5000, True),
+    (16384, 16384, False), (131072, 4096, True), (3000, 2999, False),
+])
+def test_topk_gather_ties_and_specials(L, l, specials):
+    """Bit-exact selection on tie-heavy scores with -inf/+inf/-0/+0/NaN, LDS and global paths."""
+    Hkv, d = 3, 64
+    s = synth.tie_heavy_scores(Hkv, L, seed=L + l, specials=specials)
+    k = synth.random_bf16((L, Hkv, d), 8, stream=L)
+    v = synth.random_bf16((L, Hkv, d), 9, stream=L)
+    pr = B.Problem(Hkv, Hkv, d, L, 0, l, 1, 2, None)
+    idx, kc, vc = B.apb_topk_gather(pr, to_device_f32(s), to_device_bf16(k), to_device_bf16(v))
+    torch.cuda.synchronize()
+    idx_np = _np(idx)
+    assert np.array_equal(idx_np, orc.topl(s, l))
+    kr, vr = orc.gather(k, v, idx_np)
+    assert np.array_equal(from_device_bf16(kc), kr) and np.array_equal(from_device_bf16(vc), vr)
+
+
+def test_build_passing_many_hosts():
+    """p = 130 earlier hosts: more than one launch of the batched copy."""
+    p, l, Hkv, d = 130, 3, 2, 64
+    blocks = [(synth.random_bf16((l, Hkv, d), 10, stream=j), synth.random_bf16((l, Hkv, d), 11, stream=j))
+              for j in range(p)]
+    pr = B.Problem(Hkv, Hkv, d, 8, 0, l, p, p + 1, None)
+    kp, vp = B.apb_build_passing(pr, [to_device_bf16(b[0]) for b in blocks],
+                                 [to_device_bf16(b[1]) for b in blocks])
+    torch.cuda.synchronize()
+    kr, vr = orc.build_passing([b[0] for b in blocks], [b[1] for b in blocks])
+    assert np.array_equal(from_device_bf16(kp), kr) and np.array_equal(from_device_bf16(vp), vr)
+
+
+def test_outputs_fully_written_no_overrun_and_deterministic():
+    """NaN-filled outputs inside guard bands: every element written, guards intact, bits repeat."""
+    L, A, P, Hq, Hkv, d = 300, 64, 96, 4, 2, 128
+    pr = B.Problem(Hq, Hkv, d, L, A, 32, 3, 4, None)
+    ins = [synth.random_bf16(s, 20 + i) for i, s in enumerate(
+        [(L, Hq, d), (A, Hkv, d), (A, Hkv, d), (P, Hkv, d), (P, Hkv, d), (L, Hkv, d), (L, Hkv, d)])]
+    dev = [to_device_bf16(x) for x in ins]
+    G = 64
+    n_out = L * Hq * d
+    backing = torch.full((n_out + 2 * G,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse_backing = torch.full((Hq * L + 2 * G,), float("nan"), dtype=torch.float32, device="cuda")
+    out = backing[G:G + n_out].view(L, Hq, d)
+    lse = lse_backing[G:G + Hq * L].view(Hq, L)
+    B.apb_block_attention(pr, *dev, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(backing[:G]).all() and torch.isnan(backing[G + n_out:]).all()
+    assert torch.isnan(lse_backing[:G]).all() and torch.isnan(lse_backing[G + Hq * L:]).all()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    first = out.clone(), lse.clone()
+    for _ in range(3):
+        B.apb_block_attention(pr, *dev, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), first[0].view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), first[1].view(torch.int32))
