@@ -7,11 +7,11 @@
 // passing token preceding every local token in the sequence.
 //
 // gfx950 design (one code path, instantiated for head_dim 64 and 128):
-//  * Workgroup = 4 wave64s; each wave owns 32*NSUB consecutive query rows of one
+//  * Workgroup = NW wave64s; each wave owns 32*NSUB consecutive query rows of one
 //    q head.  The grid walks (kv head, q tile longest-first, q head of the group)
 //    and is remapped so that consecutive work items land on the same XCD: the q
 //    heads sharing a kv head stream the same K/V tiles through one L2.
-//  * K/V tiles of 64 keys are staged through double-buffered LDS with register
+//  * K/V tiles of BN keys are staged through double-buffered LDS with register
 //    prefetch of the next tile; one barrier per tile.  Segment tails and the
 //    causal diagonal are masked; local tiles beyond a wave's last row are skipped.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the query row is the MFMA column,
@@ -25,14 +25,29 @@
 //    bank conflicts.
 //  * Online softmax in the exp2 domain with the scale folded into one FMA; the
 //    row max is exchanged between lane halves with v_permlane32_swap; the row
-//    sum stays per lane until the end.
+//    sum stays per lane until the end.  The running max is only moved when a
+//    row's max grows by more than 2^8 (then O and the sum are rescaled); until
+//    then probabilities are taken against the stale max, which is exact after
+//    the final normalisation and keeps every p below 2^8.
 #include "apb_internal.h"
+
+#ifndef APB_ATTN_NSUB
+#define APB_ATTN_NSUB 1
+#endif
+#ifndef APB_ATTN_BN
+#define APB_ATTN_BN 64
+#endif
+#ifndef APB_ATTN_NW
+#define APB_ATTN_NW 8
+#endif
+#ifndef APB_ATTN_WPE
+#define APB_ATTN_WPE 2
+#endif
 
 namespace apb {
 namespace {
 
-constexpr int kBN = 64;       // keys per tile
-constexpr int kThreads = 256;
+constexpr float kLazyRescale = 8.0f;  // log2 units
 
 __device__ __forceinline__ float half_swap_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -44,12 +59,12 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS slot of key row `row` (0..63) of a K tile: slot m of a 32-row block holds
+// LDS slot of key row `row` of a K tile: within each 32-row block, slot m holds
 // key ((m%8)/4)*16 + (m/8)*4 + m%4, so MFMA output value i of lane half h is
-// key 16h + i.
+// key 16h + i of the block.
 __device__ __forceinline__ int k_slot(int row) {
   const int r = row & 31;
-  return (row & 32) + ((r & 15) >> 2) * 8 + (r >> 4) * 4 + (r & 3);
+  return (row & ~31) + ((r & 15) >> 2) * 8 + (r >> 4) * 4 + (r & 3);
 }
 
 // 16-byte chunk swizzle of the transposed V tile (row = head-dim index).
@@ -77,19 +92,31 @@ struct TileRef {
   int k0, seg_len, seg;  // seg: 0 anchor, 1 passing, 2 local
 };
 
-template <int D, int NSUB>
-__global__ __launch_bounds__(kThreads) void block_attention_kernel(const AttnArgs a) {
-  constexpr int BM = 4 * 32 * NSUB;        // query rows per workgroup
-  constexpr int KP = D + 8;                // K row pitch in u16 (16 B pad)
-  constexpr int KS = kBN * KP;             // K tile, u16
-  constexpr int VS = D * kBN;              // transposed V tile, u16
-  constexpr int CH = D / 8;                // 16-byte chunks per row
-  constexpr int KROWS = kThreads / CH;     // K rows loaded per pass
-  constexpr int KIT = kBN / KROWS;         // K passes per thread
-  constexpr int KPT = kBN * CH / kThreads; // V keys per thread
-  constexpr int DB = D / 32;               // 32-wide head-dim blocks of O
-  constexpr int KK = D / 16;               // MFMA k-steps over head_dim
-  static_assert(KPT == 2 || KPT == 4, "V transpose expects 2 or 4 keys per thread");
+template <int D, int NSUB, int BN, int NW>
+struct AttnCfg {
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int BM = NW * 32 * NSUB;      // query rows per workgroup
+  static constexpr int KP = D + 8;               // K row pitch in u16 (16 B pad)
+  static constexpr int KS = BN * KP;             // K tile, u16
+  static constexpr int VS = D * BN;              // transposed V tile, u16
+  static constexpr int CH = D / 8;               // 16-byte chunks per row
+  static constexpr int KROWS = kThreads / CH;    // K rows loaded per pass
+  static constexpr int KIT = BN / KROWS;         // K passes per thread
+  static constexpr int KPT = BN * CH / kThreads; // V keys per thread
+  static constexpr int NKB = BN / 32;            // 32-key blocks per tile
+  static constexpr int DB = D / 32;              // 32-wide head-dim blocks of O
+  static constexpr int KK = D / 16;              // MFMA k-steps over head_dim
+  static constexpr int LDS_BYTES = 2 * (KS + VS) * 2;
+  static_assert(KPT == 2 || KPT == 4 || KPT == 8, "V transpose expects 2, 4 or 8 keys per thread");
+  static_assert(KIT >= 1 && KROWS * KIT == BN, "K tile split");
+};
+
+template <int D, int NSUB, int BN, int NW, int WPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
+void block_attention_kernel(const AttnArgs a) {
+  using C = AttnCfg<D, NSUB, BN, NW>;
+  constexpr int BM = C::BM, KP = C::KP, KS = C::KS, VS = C::VS, CH = C::CH, KROWS = C::KROWS;
+  constexpr int KIT = C::KIT, KPT = C::KPT, NKB = C::NKB, DB = C::DB, KK = C::KK;
 
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KS + VS)];
 
@@ -130,20 +157,20 @@ __global__ __launch_bounds__(kThreads) void block_attention_kernel(const AttnArg
   }
 
   // ---- tile list: anchor tiles, passing tiles, local tiles up to the last row
-  const int nA = (a.A + kBN - 1) / kBN;
-  const int nP = (a.P + kBN - 1) / kBN;
+  const int nA = (a.A + BN - 1) / BN;
+  const int nP = (a.P + BN - 1) / BN;
   const int last_row = min(r0 + BM, a.L);
-  const int nL = (last_row + kBN - 1) / kBN;
+  const int nL = (last_row + BN - 1) / BN;
   const int n_tiles = nA + nP + nL;
 
   auto tile_ref = [&](int t) {
     TileRef r;
     if (t < nA) {
-      r.k = a.ka; r.v = a.va; r.k0 = t * kBN; r.seg_len = a.A; r.seg = 0;
+      r.k = a.ka; r.v = a.va; r.k0 = t * BN; r.seg_len = a.A; r.seg = 0;
     } else if (t < nA + nP) {
-      r.k = a.kp; r.v = a.vp; r.k0 = (t - nA) * kBN; r.seg_len = a.P; r.seg = 1;
+      r.k = a.kp; r.v = a.vp; r.k0 = (t - nA) * BN; r.seg_len = a.P; r.seg = 1;
     } else {
-      r.k = a.kl; r.v = a.vl; r.k0 = (t - nA - nP) * kBN; r.seg_len = a.L; r.seg = 2;
+      r.k = a.kl; r.v = a.vl; r.k0 = (t - nA - nP) * BN; r.seg_len = a.L; r.seg = 2;
     }
     return r;
   };
@@ -186,8 +213,15 @@ __global__ __launch_bounds__(kThreads) void block_attention_kernel(const AttnArg
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int d = chunk * 8 + e;
-      uint16_t *dst = Vt + d * kBN + (((key0 >> 3) ^ v_swz(d)) << 3) + (key0 & 7);
-      if constexpr (KPT == 4) {
+      uint16_t *dst = Vt + d * BN + (((key0 >> 3) ^ v_swz(d)) << 3) + (key0 & 7);
+      if constexpr (KPT == 8) {
+        uint4 p;
+        p.x = pack2(u16_at(vreg[0], e), u16_at(vreg[1], e));
+        p.y = pack2(u16_at(vreg[2], e), u16_at(vreg[3], e));
+        p.z = pack2(u16_at(vreg[4], e), u16_at(vreg[5], e));
+        p.w = pack2(u16_at(vreg[6], e), u16_at(vreg[7], e));
+        *reinterpret_cast<uint4 *>(dst) = p;
+      } else if constexpr (KPT == 4) {
         uint2 p;
         p.x = pack2(u16_at(vreg[0], e), u16_at(vreg[1], e));
         p.y = pack2(u16_at(vreg[2], e), u16_at(vreg[3], e));
@@ -226,12 +260,14 @@ __global__ __launch_bounds__(kThreads) void block_attention_kernel(const AttnArg
     const uint16_t *Vt = Ks + KS;
     const bool wave_active = !(cur.seg == 2 && cur.k0 > rw + 32 * NSUB - 1);
     if (wave_active) {
-      // S^T = K Q^T for two 32-key blocks
-      f32x16 sacc[NSUB][2];
+      // S^T = K Q^T, one 32-key block at a time
+      f32x16 sacc[NSUB][NKB];
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) { sacc[s][0] = f32x16{}; sacc[s][1] = f32x16{}; }
+      for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) sacc[s][kb] = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + (kb * 32 + lrow) * KP + kk * 16 + half * 8);
@@ -241,14 +277,14 @@ __global__ __launch_bounds__(kThreads) void block_attention_kernel(const AttnArg
         }
       }
 
-      const bool need_mask = (cur.k0 + kBN > cur.seg_len) || (cur.seg == 2 && cur.k0 + kBN - 1 > rw);
-      bf16x8 pf[NSUB][2][2];
+      const bool need_mask = (cur.k0 + BN > cur.seg_len) || (cur.seg == 2 && cur.k0 + BN - 1 > rw);
+      bf16x8 pf[NSUB][NKB][2];
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
         if (need_mask) {
           const int row = rw + s * 32 + lrow;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
+          for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int key = cur.k0 + kb * 32 + half * 16 + i;
@@ -259,17 +295,23 @@ __global__ __launch_bounds__(kThreads) void block_attention_kernel(const AttnArg
         }
         float mx = sacc[s][0][0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[s][0][i]);
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[s][1][i]);
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[s][kb][i]);
         mx = half_swap_max(mx);
-        const float m_new = fmaxf(m_run[s], mx * sl2);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_use);
-        m_run[s] = m_new;
+        const float m_cand = fmaxf(m_run[s], mx * sl2);
+        const bool grow = m_cand > m_run[s] + kLazyRescale;
+        if (__ballot(grow)) {
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[s] - m_cand) : 1.f;
+          m_run[s] = grow ? m_cand : m_run[s];
+          l_run[s] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[s][db] *= alpha;
+        }
+        const float m_use = (m_run[s] == -INFINITY) ? 0.f : m_run[s];
         float psum = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             uint32_t w4[4];
@@ -283,21 +325,19 @@ __global__ __launch_bounds__(kThreads) void block_attention_kernel(const AttnArg
             pf[s][kb][c] = __builtin_bit_cast(bf16x8, (uint4{w4[0], w4[1], w4[2], w4[3]}));
           }
         }
-        l_run[s] = l_run[s] * alpha + psum;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[s][db] *= alpha;
+        l_run[s] += psum;
       }
 
       // O^T += V^T P^T
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const int lchunk = kb * 4 + half * 2 + c;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
             const int d = db * 32 + lrow;
-            const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vt + d * kBN + ((lchunk ^ v_swz(d)) << 3));
+            const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vt + d * BN + ((lchunk ^ v_swz(d)) << 3));
 #pragma unroll
             for (int s = 0; s < NSUB; ++s)
               acc[s][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s][kb][c], acc[s][db], 0, 0, 0);
@@ -335,21 +375,21 @@ __global__ __launch_bounds__(kThreads) void block_attention_kernel(const AttnArg
   }
 }
 
-template <int D, int NSUB>
+template <int D, int NSUB, int BN, int NW, int WPE>
 hipError_t launch_impl(AttnArgs &a, hipStream_t s) {
-  constexpr int BM = 4 * 32 * NSUB;
-  a.n_qtiles = (a.L + BM - 1) / BM;
+  using C = AttnCfg<D, NSUB, BN, NW>;
+  a.n_qtiles = (a.L + C::BM - 1) / C::BM;
   a.n_work = a.n_qtiles * a.Hq;
   const int grid = (a.n_work + kNumXcd - 1) / kNumXcd * kNumXcd;
-  hipLaunchKernelGGL((block_attention_kernel<D, NSUB>), dim3(grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((block_attention_kernel<D, NSUB, BN, NW, WPE>), dim3(grid), dim3(C::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_block_attention(AttnArgs &a, int head_dim, hipStream_t s) {
-  if (head_dim == 128) return launch_impl<128, 1>(a, s);
-  return launch_impl<64, 1>(a, s);
+  if (head_dim == 128) return launch_impl<128, APB_ATTN_NSUB, APB_ATTN_BN, APB_ATTN_NW, APB_ATTN_WPE>(a, s);
+  return launch_impl<64, 1, 64, 4, 2>(a, s);
 }
 
 }  // namespace apb
