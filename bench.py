@@ -125,6 +125,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before warm-up, run one plain device-to-device copy of this many MiB "
+                         "(a known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the per-host path has no collective in this build "
@@ -168,6 +171,14 @@ def main():
     torch.cuda.synchronize()
     buf = pipeline.StepBuffers.allocate(pr)
     stream = torch.cuda.current_stream()
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print("# warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         pipeline.host_step(pr, sc, host, ka, va, kcs, vcs, buf, stream=stream)

@@ -11,24 +11,28 @@
 //    q head.  The grid walks (kv head, q tile longest-first, q head of the group)
 //    and is remapped so that consecutive work items land on the same XCD: the q
 //    heads sharing a kv head stream the same K/V tiles through one L2.
-//  * K/V tiles of BN keys are staged through double-buffered LDS with register
-//    prefetch of the next tile; one barrier per tile.  Segment tails and the
-//    causal diagonal are masked; local tiles beyond a wave's last row are skipped.
+//  * K/V tiles of BN keys go HBM -> LDS by LDS-DMA (buffer_load_dwordx4 ... lds):
+//    no staging registers, no LDS store instructions, and per-lane source offsets
+//    fixed for the whole kernel.  A per-tile buffer descriptor ends at the
+//    segment's last row, so rows past it read as zeros.  Two LDS buffers: tile
+//    t+1 lands while tile t is consumed; one barrier per tile.  Segment tails and
+//    the causal diagonal are masked; local tiles past a wave's rows are skipped.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the query row is the MFMA column,
 //    so each lane holds the scores of one row (16 keys per 32-key block).  K rows
-//    are stored in LDS in a permuted order chosen so that lane half h of the
-//    accumulator holds keys 16h..16h+15 of the block, in order.  Those 16 values,
-//    converted to bf16, are directly the B operand of O^T = V^T P^T: no
-//    cross-lane movement of P.
-//  * V is transposed into LDS (rows = head_dim) with a 16-byte XOR swizzle so
-//    that both the transposing writes and the MFMA operand reads are free of
-//    bank conflicts.
-//  * Online softmax in the exp2 domain with the scale folded into one FMA; the
-//    row max is exchanged between lane halves with v_permlane32_swap; the row
-//    sum stays per lane until the end.  The running max is only moved when a
-//    row's max grows by more than 2^8 (then O and the sum are rescaled); until
-//    then probabilities are taken against the stale max, which is exact after
-//    the final normalisation and keeps every p below 2^8.
+//    sit in LDS in a permuted slot order chosen so that lane half h of the
+//    accumulator holds keys 16h..16h+15 of the block, in order; those values,
+//    converted to bf16, are directly the B operand of O^T = V^T P^T (no lane
+//    movement of P).  16-byte chunks of a K row are XOR-swizzled by the slot.
+//  * V stays row-major in LDS (32-byte granules XOR-swizzled by key) and the A
+//    operand of O^T = V^T P^T is read with ds_read_b64_tr_b16, which transposes
+//    4 keys x 16 head-dim values across each 16-lane group.
+//  * Online softmax in the exp2 domain with the scale folded into one FMA.  The
+//    common path has no row max: probabilities are taken against the running
+//    reference, and only a wave in which some lane's tile sum exceeds 2^32 (or is
+//    not finite, as on the first tile) computes the true max, rescales O and the
+//    sum, and recomputes.  The final normalisation makes this exact; every p
+//    stays far below the fp32 and bf16 range.  The row max is exchanged between
+//    lane halves with v_permlane32_swap; row sums stay per lane until the end.
 #include "apb_internal.h"
 
 #ifndef APB_ATTN_NSUB
@@ -46,8 +50,6 @@
 
 namespace apb {
 namespace {
-
-constexpr float kLazyRescale = 8.0f;  // log2 units
 
 __device__ __forceinline__ float half_swap_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -67,18 +69,6 @@ __device__ __forceinline__ int k_slot(int row) {
   return (row & ~31) + ((r & 15) >> 2) * 8 + (r >> 4) * 4 + (r & 3);
 }
 
-// 16-byte chunk swizzle of the transposed V tile (row = head-dim index).
-__device__ __forceinline__ int v_swz(int d) { return (d ^ (d >> 3)) & 7; }
-
-__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) {
-  return (lo16 & 0xffffu) | (hi16 << 16);
-}
-
-__device__ __forceinline__ uint32_t u16_at(const uint4 &x, int e) {
-  const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
 __device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 p;
@@ -92,33 +82,67 @@ struct TileRef {
   int k0, seg_len, seg;  // seg: 0 anchor, 1 passing, 2 local
 };
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Inverse of k_slot: key row stored in LDS slot `slot` of a K tile.
+__device__ __forceinline__ int slot_key(int slot) {
+  const int u = slot & 31;
+  return (slot & ~31) + ((u & 7) >> 2) * 16 + (u >> 3) * 4 + (u & 3);
+}
+
 template <int D, int NSUB, int BN, int NW>
 struct AttnCfg {
   static constexpr int kThreads = 64 * NW;
   static constexpr int BM = NW * 32 * NSUB;      // query rows per workgroup
-  static constexpr int KP = D + 8;               // K row pitch in u16 (16 B pad)
-  static constexpr int KS = BN * KP;             // K tile, u16
-  static constexpr int VS = D * BN;              // transposed V tile, u16
+  static constexpr int ROWB = D * 2;             // bytes per K/V row in LDS (no padding)
+  static constexpr int TILE_BYTES = BN * ROWB;   // one K or V tile
   static constexpr int CH = D / 8;               // 16-byte chunks per row
-  static constexpr int KROWS = kThreads / CH;    // K rows loaded per pass
-  static constexpr int KIT = BN / KROWS;         // K passes per thread
-  static constexpr int KPT = BN * CH / kThreads; // V keys per thread
+  static constexpr int GR = D / 16;              // 32-byte granules per row
+  static constexpr int KI = TILE_BYTES / 1024 / NW;  // 1 KB LDS-DMA loads per wave per tile
   static constexpr int NKB = BN / 32;            // 32-key blocks per tile
   static constexpr int DB = D / 32;              // 32-wide head-dim blocks of O
   static constexpr int KK = D / 16;              // MFMA k-steps over head_dim
-  static constexpr int LDS_BYTES = 2 * (KS + VS) * 2;
-  static_assert(KPT == 2 || KPT == 4 || KPT == 8, "V transpose expects 2, 4 or 8 keys per thread");
-  static_assert(KIT >= 1 && KROWS * KIT == BN, "K tile split");
+  static_assert(KI >= 1 && KI * 1024 * NW == TILE_BYTES, "tile split over LDS-DMA loads");
 };
+
+// V tile granule swizzle: 32-byte granule g of key row `key` sits at g ^ vsw(key).
+template <int GR>
+__device__ __forceinline__ int vsw(int key) { return (2 * (key & 3)) & (GR - 1); }
+
+// Issue this wave's LDS-DMA loads of one K tile and one V tile (KI x 1 KB each).
+// The buffer descriptors cover rows [k0, seg_len) of the segment (at most BN), so
+// rows past a segment's end read as zeros.  (The body exists only in the device
+// pass: the host pass has no buffer-descriptor type.)
+template <int KI, int BN>
+__device__ __forceinline__ void issue_tile_loads(const TileRef &t, int kv_row_bytes, uint8_t *kdst, uint8_t *vdst,
+                                                 const int (&koff)[KI], const int (&voff)[KI]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int valid_bytes = min(t.seg_len - t.k0, BN) * kv_row_bytes;
+  const size_t base = (size_t)t.k0 * (size_t)(kv_row_bytes / 2);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(t.k + base), 0, valid_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(t.v + base), 0, valid_bytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(kdst + i * 1024), 16, koff[i], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vdst + i * 1024), 16, voff[i], 0, 0, 0);
+  }
+#endif
+}
+
+constexpr float kRescaleSum = 4294967296.0f;  // 2^32: a tile sum above this moves the max
 
 template <int D, int NSUB, int BN, int NW, int WPE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, 8)))
 void block_attention_kernel(const AttnArgs a) {
   using C = AttnCfg<D, NSUB, BN, NW>;
-  constexpr int BM = C::BM, KP = C::KP, KS = C::KS, VS = C::VS, CH = C::CH, KROWS = C::KROWS;
-  constexpr int KIT = C::KIT, KPT = C::KPT, NKB = C::NKB, DB = C::DB, KK = C::KK;
+  constexpr int BM = C::BM, ROWB = C::ROWB, TB = C::TILE_BYTES, CH = C::CH, GR = C::GR, KI = C::KI;
+  constexpr int NKB = C::NKB, DB = C::DB, KK = C::KK;
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KS + VS)];
+  // [buffer][K tile | V tile]
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TB];
 
   // ---- work item: XCD-aware remap, then (kv head, q tile longest-first, member)
   const int nb = gridDim.x;
@@ -139,7 +163,10 @@ void block_attention_kernel(const AttnArgs a) {
   const int r0 = qtile * BM;
   const int rw = r0 + wave * 32 * NSUB;   // first row of this wave
   const size_t q_stride = (size_t)a.Hq * D;
-  const size_t kv_stride = (size_t)a.Hkv * D;
+  const int kv_row_bytes = a.Hkv * D * 2;
+
+  // ---- zero both LDS buffers once: rows past a segment end never hold NaN
+  for (int i = tid; i < 2 * 2 * TB / 16; i += C::kThreads) reinterpret_cast<uint4 *>(smem)[i] = uint4{0, 0, 0, 0};
 
   // ---- Q fragments (B operand of S^T = K Q^T): row lrow, head-dim 16kk + 8half..+7
   bf16x8 qf[NSUB][KK];
@@ -154,6 +181,22 @@ void block_attention_kernel(const AttnArgs a) {
         qf[s][kk] = bf16x8{};
       }
     }
+  }
+
+  // ---- per-lane source offsets of the LDS-DMA loads (fixed for the whole kernel).
+  // Load i of this wave fills LDS bytes [(wave*KI + i) * 1024, +1024) of a tile;
+  // lane p writes 16 bytes at p*16 of that range.
+  int koff[KI], voff[KI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int pos = (wave * KI + i) * 64 + lane;  // 16-byte position in the tile
+    const int row = pos / CH;
+    const int pc = pos % CH;
+    // K: LDS row `row` is slot `row`, holding key slot_key(row); chunk pc holds chunk pc ^ (row % CH).
+    koff[i] = slot_key(row) * kv_row_bytes + h * D * 2 + ((pc ^ (row & (CH - 1))) * 16);
+    // V: LDS row = key; granule pc/2 holds granule (pc/2) ^ vsw(key).
+    const int gi = (pc >> 1) ^ vsw<GR>(row);
+    voff[i] = row * kv_row_bytes + h * D * 2 + (gi * 2 + (pc & 1)) * 16;
   }
 
   // ---- tile list: anchor tiles, passing tiles, local tiles up to the last row
@@ -175,62 +218,19 @@ void block_attention_kernel(const AttnArgs a) {
     return r;
   };
 
-  uint4 kreg[KIT];
-  uint4 vreg[KPT];
-  const int chunk = tid % CH;
-  const int kg = tid / CH;
-
-  auto load_regs = [&](const TileRef &t) {
+  // ---- per-lane LDS read offsets
+  // K (A operand of S^T): slot kb*32 + lrow, chunk (2kk + half) ^ (lrow % CH)
+  const int k_rd = lrow * ROWB;
+  const int k_x = lrow & (CH - 1);
+  // V (A operand of O^T via the transposing read): 16-lane group gq reads keys
+  // base + (lane%16)/4 at head-dim db*32 + (gq%2)*16 + 4*(lane%4) .. +3.
+  const int gq = lane >> 4;
+  const int v_key = half * 16 + ((lane & 15) >> 2);
+  const int v_fx = vsw<GR>(v_key);
+  int v_rd[DB];
 #pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int key = t.k0 + it * KROWS + kg;
-      if (key < t.seg_len) {
-        kreg[it] = *reinterpret_cast<const uint4 *>(t.k + key * kv_stride + h * D + chunk * 8);
-      } else {
-        kreg[it] = uint4{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int key = t.k0 + kg * KPT + j;
-      if (key < t.seg_len) {
-        vreg[j] = *reinterpret_cast<const uint4 *>(t.v + key * kv_stride + h * D + chunk * 8);
-      } else {
-        vreg[j] = uint4{0, 0, 0, 0};
-      }
-    }
-  };
-
-  auto store_lds = [&](uint16_t *buf) {
-    uint16_t *Ks = buf;
-    uint16_t *Vt = buf + KS;
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int row = it * KROWS + kg;
-      *reinterpret_cast<uint4 *>(Ks + k_slot(row) * KP + chunk * 8) = kreg[it];
-    }
-    const int key0 = kg * KPT;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = chunk * 8 + e;
-      uint16_t *dst = Vt + d * BN + (((key0 >> 3) ^ v_swz(d)) << 3) + (key0 & 7);
-      if constexpr (KPT == 8) {
-        uint4 p;
-        p.x = pack2(u16_at(vreg[0], e), u16_at(vreg[1], e));
-        p.y = pack2(u16_at(vreg[2], e), u16_at(vreg[3], e));
-        p.z = pack2(u16_at(vreg[4], e), u16_at(vreg[5], e));
-        p.w = pack2(u16_at(vreg[6], e), u16_at(vreg[7], e));
-        *reinterpret_cast<uint4 *>(dst) = p;
-      } else if constexpr (KPT == 4) {
-        uint2 p;
-        p.x = pack2(u16_at(vreg[0], e), u16_at(vreg[1], e));
-        p.y = pack2(u16_at(vreg[2], e), u16_at(vreg[3], e));
-        *reinterpret_cast<uint2 *>(dst) = p;
-      } else {
-        *reinterpret_cast<uint32_t *>(dst) = pack2(u16_at(vreg[0], e), u16_at(vreg[1], e));
-      }
-    }
-  };
+  for (int db = 0; db < DB; ++db)
+    v_rd[db] = v_key * ROWB + (((db * 2 + (gq & 1)) ^ v_fx) * 32) + (lane & 3) * 8;
 
   // ---- accumulators
   f32x16 acc[NSUB][DB];
@@ -245,19 +245,21 @@ void block_attention_kernel(const AttnArgs a) {
   const float sl2 = a.scale_log2;
 
   // ---- prologue
-  {
-    TileRef t0 = tile_ref(0);
-    load_regs(t0);
-    store_lds(smem);
-    __syncthreads();
-  }
+  __syncthreads();  // LDS zeroed before the first DMA lands
+  issue_tile_loads<KI, BN>(tile_ref(0), kv_row_bytes, smem + wave * KI * 1024, smem + TB + wave * KI * 1024,
+                           koff, voff);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
     const TileRef cur = tile_ref(t);
-    if (t + 1 < n_tiles) load_regs(tile_ref(t + 1));
+    if (t + 1 < n_tiles) {
+      uint8_t *kdst = smem + ((t + 1) & 1) * 2 * TB + wave * KI * 1024;
+      issue_tile_loads<KI, BN>(tile_ref(t + 1), kv_row_bytes, kdst, kdst + TB, koff, voff);
+    }
 
-    const uint16_t *Ks = smem + (t & 1) * (KS + VS);
-    const uint16_t *Vt = Ks + KS;
+    const uint8_t *Ks = smem + (t & 1) * 2 * TB;
+    const uint8_t *Vs = Ks + TB;
     const bool wave_active = !(cur.seg == 2 && cur.k0 > rw + 32 * NSUB - 1);
     if (wave_active) {
       // S^T = K Q^T, one 32-key block at a time
@@ -270,7 +272,7 @@ void block_attention_kernel(const AttnArgs a) {
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + (kb * 32 + lrow) * KP + kk * 16 + half * 8);
+          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + kb * 32 * ROWB + k_rd + (((2 * kk + half) ^ k_x) * 16));
 #pragma unroll
           for (int s = 0; s < NSUB; ++s)
             sacc[s][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s][kk], sacc[s][kb], 0, 0, 0);
@@ -293,51 +295,60 @@ void block_attention_kernel(const AttnArgs a) {
             }
           }
         }
-        float mx = sacc[s][0][0];
+        // Probabilities against the running reference m_run; a wave whose tile sum
+        // is too large (or not finite, as on the first tile) moves the reference to
+        // the true max, rescales O and the sum, and recomputes.
+        auto exp_tile = [&](float m_use) {
+          float psum = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+          for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[s][kb][i]);
-        mx = half_swap_max(mx);
-        const float m_cand = fmaxf(m_run[s], mx * sl2);
-        const bool grow = m_cand > m_run[s] + kLazyRescale;
-        if (__ballot(grow)) {
-          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[s] - m_cand) : 1.f;
-          m_run[s] = grow ? m_cand : m_run[s];
+            for (int c = 0; c < 2; ++c) {
+              uint32_t w4[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s][kb][c * 8 + 2 * j], sl2, -m_use));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s][kb][c * 8 + 2 * j + 1], sl2, -m_use));
+                psum += p0 + p1;
+                w4[j] = bf16x2_bits(p0, p1);
+              }
+              pf[s][kb][c] = __builtin_bit_cast(bf16x8, (uint4{w4[0], w4[1], w4[2], w4[3]}));
+            }
+          }
+          return psum;
+        };
+        float psum = exp_tile(m_run[s]);
+        if (__ballot(!(psum <= kRescaleSum))) {
+          float mx = sacc[s][0][0];
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[s][kb][i]);
+          mx = half_swap_max(mx);
+          const float m_new = fmaxf(m_run[s], mx * sl2);
+          const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+          const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_use);
+          m_run[s] = m_new;
           l_run[s] *= alpha;
 #pragma unroll
           for (int db = 0; db < DB; ++db) acc[s][db] *= alpha;
-        }
-        const float m_use = (m_run[s] == -INFINITY) ? 0.f : m_run[s];
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            uint32_t w4[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s][kb][c * 8 + 2 * j], sl2, -m_use));
-              const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s][kb][c * 8 + 2 * j + 1], sl2, -m_use));
-              psum += p0 + p1;
-              w4[j] = bf16x2_bits(p0, p1);
-            }
-            pf[s][kb][c] = __builtin_bit_cast(bf16x8, (uint4{w4[0], w4[1], w4[2], w4[3]}));
-          }
+          psum = exp_tile(m_use);
         }
         l_run[s] += psum;
       }
 
-      // O^T += V^T P^T
+      // O^T += V^T P^T; A operand = 8 keys x 32 head-dim rows from two transposing reads
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const int lchunk = kb * 4 + half * 2 + c;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const int d = db * 32 + lrow;
-            const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vt + d * BN + ((lchunk ^ v_swz(d)) << 3));
+            const uint8_t *vb = Vs + (kb * 32 + c * 8) * ROWB + v_rd[db];
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(vb));
+            const v4i16 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(vb + 4 * ROWB));
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, (__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
 #pragma unroll
             for (int s = 0; s < NSUB; ++s)
               acc[s][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s][kb][c], acc[s][db], 0, 0, 0);
@@ -346,7 +357,7 @@ void block_attention_kernel(const AttnArgs a) {
       }
     }
 
-    if (t + 1 < n_tiles) store_lds(smem + ((t + 1) & 1) * (KS + VS));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
