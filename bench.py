@@ -76,7 +76,7 @@ def measured_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, blocks, weights, anchor, n_rows=128):
+def cpu_baseline(w, blocks, weights, anchor, n_rows=4096):
     """Time the CPU oracle on a bounded sample of one host step; scale to tokens/s."""
     from oracle import apb_oracle as orc
     from sparse_block_attention_amd import synth
@@ -121,8 +121,8 @@ def cpu_baseline(w, blocks, weights, anchor, n_rows=128):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
