@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "apb.h"
+
 namespace apb {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -12,6 +14,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Number of XCDs on MI355X; workgroups are dispatched to them round-robin.
 constexpr int kNumXcd = 8;
+
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave stay
+// outstanding.  The builtin (not inline asm) lets the compiler see the wait, so
+// it knows which loads have landed.  gfx9 immediate: vmcnt in bits 3:0 and
+// 15:14; expcnt (bits 6:4) and lgkmcnt (bits 11:8) at their maximum, i.e. not
+// waited on.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that leaves LDS-DMA loads in flight.  __syncthreads() is
+// also a workgroup memory fence, for which the compiler drains every outstanding
+// vector-memory operation, including prefetches meant to stay in flight across
+// the barrier.  Callers wait (wait_vmcnt) for exactly the LDS-DMA data they
+// need before this barrier; the barrier itself drains this wave's LDS reads,
+// so a buffer everyone has finished reading may be overwritten after it.
+__device__ __forceinline__ void barrier_keep_dma() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Attention over [anchor | passing | local causal].
 struct AttnArgs {

@@ -14,8 +14,9 @@
 //  * K/V tiles of BN keys go HBM -> LDS by LDS-DMA (buffer_load_dwordx4 ... lds):
 //    no staging registers, no LDS store instructions, and per-lane source offsets
 //    fixed for the whole kernel.  A per-tile buffer descriptor ends at the
-//    segment's last row, so rows past it read as zeros.  Two LDS buffers: tile
-//    t+1 lands while tile t is consumed; one barrier per tile.  Segment tails and
+//    segment's last row, so rows past it read as zeros.  PD+1 LDS buffers: tiles
+//    t+1..t+PD are in flight while tile t is consumed (the DMA has PD tiles of
+//    compute to land); one barrier per tile.  Segment tails and
 //    the causal diagonal are masked; local tiles past a wave's rows are skipped.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the query row is the MFMA column,
 //    so each lane holds the scores of one row (16 keys per 32-key block).  K rows
@@ -46,6 +47,12 @@
 #endif
 #ifndef APB_ATTN_WPE
 #define APB_ATTN_WPE 2
+#endif
+#ifndef APB_ATTN_PD
+#define APB_ATTN_PD 1
+#endif
+#ifndef APB_ATTN_SCHED
+#define APB_ATTN_SCHED 1
 #endif
 
 namespace apb {
@@ -141,8 +148,10 @@ void block_attention_kernel(const AttnArgs a) {
   constexpr int BM = C::BM, ROWB = C::ROWB, TB = C::TILE_BYTES, CH = C::CH, GR = C::GR, KI = C::KI;
   constexpr int NKB = C::NKB, DB = C::DB, KK = C::KK;
 
-  // [buffer][K tile | V tile]
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TB];
+  // [buffer][K tile | V tile]; tile t uses buffer t % NBUF and tile t + PD is in
+  // flight while tile t is consumed.
+  constexpr int PD = APB_ATTN_PD, NBUF = PD + 1;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * 2 * TB];
 
   // ---- work item: XCD-aware remap, then (kv head, q tile longest-first, member)
   const int nb = gridDim.x;
@@ -166,7 +175,7 @@ void block_attention_kernel(const AttnArgs a) {
   const int kv_row_bytes = a.Hkv * D * 2;
 
   // ---- zero both LDS buffers once: rows past a segment end never hold NaN
-  for (int i = tid; i < 2 * 2 * TB / 16; i += C::kThreads) reinterpret_cast<uint4 *>(smem)[i] = uint4{0, 0, 0, 0};
+  for (int i = tid; i < NBUF * 2 * TB / 16; i += C::kThreads) reinterpret_cast<uint4 *>(smem)[i] = uint4{0, 0, 0, 0};
 
   // ---- Q fragments (B operand of S^T = K Q^T): row lrow, head-dim 16kk + 8half..+7
   bf16x8 qf[NSUB][KK];
@@ -246,20 +255,26 @@ void block_attention_kernel(const AttnArgs a) {
 
   // ---- prologue
   __syncthreads();  // LDS zeroed before the first DMA lands
-  issue_tile_loads<KI, BN>(tile_ref(0), kv_row_bytes, smem + wave * KI * 1024, smem + TB + wave * KI * 1024,
-                           koff, voff);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (int j = 0; j < PD && j < n_tiles; ++j) {
+    uint8_t *kdst = smem + j * 2 * TB + wave * KI * 1024;
+    issue_tile_loads<KI, BN>(tile_ref(j), kv_row_bytes, kdst, kdst + TB, koff, voff);
+  }
+  wait_vmcnt<0>();
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
+  int buf = 0;  // t % NBUF
+  // One tile: prefetch tile t+PD into `nxt`, consume tile t from `cur`.  The two
+  // buffers are distinct; saying so (__restrict__) lets the compiler skip the
+  // wait for the in-flight DMA before reading `cur`.
+  auto tile_step = [&](int t, const uint8_t *__restrict__ cur_buf, uint8_t *__restrict__ nxt, bool prefetch) {
     const TileRef cur = tile_ref(t);
-    if (t + 1 < n_tiles) {
-      uint8_t *kdst = smem + ((t + 1) & 1) * 2 * TB + wave * KI * 1024;
-      issue_tile_loads<KI, BN>(tile_ref(t + 1), kv_row_bytes, kdst, kdst + TB, koff, voff);
+    if (prefetch) {
+      uint8_t *kdst = nxt + wave * KI * 1024;
+      issue_tile_loads<KI, BN>(tile_ref(t + PD), kv_row_bytes, kdst, kdst + TB, koff, voff);
     }
 
-    const uint8_t *Ks = smem + (t & 1) * 2 * TB;
-    const uint8_t *Vs = Ks + TB;
+    const uint8_t *Ks = cur_buf;
+    const uint8_t *Vs = cur_buf + TB;
     const bool wave_active = !(cur.seg == 2 && cur.k0 > rw + 32 * NSUB - 1);
     if (wave_active) {
       // S^T = K Q^T, one 32-key block at a time
@@ -278,6 +293,16 @@ void block_attention_kernel(const AttnArgs a) {
             sacc[s][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s][kk], sacc[s][kb], 0, 0, 0);
         }
       }
+#if APB_ATTN_SCHED
+      // K reads run KK MFMAs ahead of their use
+      __builtin_amdgcn_sched_group_barrier(0x100, KK, 0);
+#pragma unroll
+      for (int i = 0; i < (NKB - 1) * KK * NSUB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i % NSUB == NSUB - 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, KK * NSUB, 0);
+#endif
 
       const bool need_mask = (cur.k0 + BN > cur.seg_len) || (cur.seg == 2 && cur.k0 + BN - 1 > rw);
       bf16x8 pf[NSUB][NKB][2];
@@ -355,10 +380,30 @@ void block_attention_kernel(const AttnArgs a) {
           }
         }
       }
+#if APB_ATTN_SCHED
+      // transposing V reads run four MFMAs ahead of their use
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+      for (int i = 0; i < NKB * 2 * DB - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NSUB, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * NSUB, 1);
+#endif
     }
+  };
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const bool prefetch = t + PD < n_tiles;
+    const int pb = (buf + PD >= NBUF) ? buf + PD - NBUF : buf + PD;
+    tile_step(t, smem + buf * 2 * TB, smem + pb * 2 * TB, prefetch);
+
+    // Tile t+1 must have landed in every wave before the barrier; the loads of
+    // tiles t+2 .. t+PD (2*KI per tile and wave) may stay in flight across it.
+    if (prefetch) wait_vmcnt<2 * KI * (PD - 1)>();
+    else wait_vmcnt<0>();
+    barrier_keep_dma();
+    buf = (buf + 1 == NBUF) ? 0 : buf + 1;
   }
 
   // ---- epilogue: normalise, write O (bf16) and LSE (natural log)

@@ -7,150 +7,306 @@
 //   x = [q[t, G_h[0]]; ...; q[t, G_h[g-1]]; k[t, h]; v[t, h]]
 //   s = w2[h] . relu(W1[h] x + b1[h]) + b2[h]
 //
-// gfx950 design: Z^T = W1 X^T on v_mfma_f32_32x32x16_bf16 (M = hidden units,
-// N = tokens, K = (g+2)d).  Each wave owns 32 tokens and every hidden unit, so
-// the ReLU and the w2 dot product finish inside the wave (one lane-half swap).
-// X is streamed from HBM straight into B-operand registers (each byte is read
-// exactly once), prefetched one 64-wide K chunk ahead; W1 chunks are staged in
-// double-buffered LDS and shared by the workgroup's 4 waves.  Work items are
-// grouped by kv head onto XCDs so a head's W1 stays in one L2.
+// gfx950 design: a workgroup takes 128 tokens of one kv head and all Hs hidden
+// units: Z^T = W1 X^T on v_mfma_f32_32x32x16_bf16 (M = hidden, N = tokens,
+// K = (g+2)d), K walked in 32-wide chunks.  Each of the 4 waves owns a quarter
+// of the hidden blocks for all 128 tokens, so a W1 element is read from LDS by
+// one wave only.  X and W1 chunks reach LDS by LDS-DMA (buffer_load ... lds)
+// through a 3-deep ring: two chunks are in flight while one is consumed, and
+// two workgroups share a CU, which keeps enough HBM reads outstanding.  Rows of
+// a chunk are 64 bytes; their 16-byte pieces are XOR-swizzled by row so the
+// MFMA operand reads are free of bank conflicts.  The epilogue adds b1, applies
+// ReLU and the w2 dot product in fp32, and sums the four waves' partial dot
+// products through LDS.  Work items are grouped by kv head onto XCDs so a
+// head's W1 stays in one L2.
+#include <stddef.h>
+
 #include "apb_internal.h"
 
 namespace apb {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTok = 128;      // tokens per workgroup (4 waves x 32)
-constexpr int kKC = 64;        // K chunk (elements of x)
-constexpr int kWP = kKC + 8;   // W1 LDS row pitch in u16
+constexpr int kThreads = 256;      // 4 waves
+constexpr int kTok = 128;          // tokens per workgroup
+constexpr int kKC = 32;            // K chunk (elements of x)
+constexpr int kRing = 3;           // LDS ring depth (chunks in flight: kRing - 1)
+constexpr int kRowB = kKC * 2;     // bytes per chunk row (64)
+constexpr int kXB = kTok * kRowB;  // X chunk bytes (8 KB)
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ float half_swap_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int HSB>  // hidden = 32 * HSB
-__global__ __launch_bounds__(kThreads) void score_kv_kernel(const ScoreArgs a) {
-  constexpr int HS = 32 * HSB;
-  constexpr int WCH = HS * kKC / 8;                 // 16-byte pieces per W1 chunk
-  constexpr int WIT = (WCH + kThreads - 1) / kThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t wbuf[2][HS * kWP];
+// 16-byte piece p of chunk row r sits at piece p ^ swz(r).
+__device__ __forceinline__ int piece_swz(int r) { return (r >> 2) & 3; }
+
+// One 1 KB LDS-DMA load (16 rows x 64 bytes).  Base and range are the same in
+// every lane; readfirstlane says so, so the descriptor lives in scalar registers.
+// (Device pass only: the host pass has no buffer-descriptor type.)
+__device__ __forceinline__ void dma_1k(const void *base, int valid_bytes, int voff, uint8_t *dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void *>(ub), 0, __builtin_amdgcn_readfirstlane(valid_bytes), 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, voff, 0, 0, 0);
+#endif
+}
+
+// A wave issues 2 X loads plus W1 loads wave, wave+4, ... < WI_TOTAL per chunk;
+// wait until only the newest chunk's loads may be outstanding.
+template <int WI_TOTAL>
+__device__ __forceinline__ void wait_all_but_newest_chunk(int wave) {
+  if constexpr (WI_TOTAL % 4 == 0) {
+    wait_vmcnt<2 + WI_TOTAL / 4>();
+  } else {
+    switch ((WI_TOTAL - wave + 3) / 4) {
+      case 0: wait_vmcnt<2>(); break;
+      case 1: wait_vmcnt<3>(); break;
+      case 2: wait_vmcnt<4>(); break;
+      case 3: wait_vmcnt<5>(); break;
+      default: wait_vmcnt<6>(); break;
+    }
+  }
+}
+
+// Where chunk c comes from.
+struct ChunkSrc {
+  const uint16_t *x;  // first element of the chunk in token row t0 of its tensor
+  int x_valid;        // bytes of valid rows from x (range of the descriptor)
+  int xo0, xo1;       // this lane's offsets for its two X loads
+  const uint16_t *w;  // W1 column offset of the chunk
+};
+
+// Per-workgroup constants needed to locate a chunk's sources.
+struct SrcCtx {
+  const uint16_t *q0, *k0, *v0;  // token row t0 of q, k, v
+  const uint16_t *w1h;           // W1 of this kv head
+  int xq_valid, xkv_valid;       // descriptor ranges for q rows and k/v rows
+  int xq0, xq1, xkv0, xkv1;      // lane offsets of the two X loads, q and k/v strides
+  int g, d;
+};
+
+// LDS reads in the main loop go through __restrict__ parameters (here and in
+// score_chunk): the alias scopes that gives them tell the compiler that the
+// LDS-DMA loads in flight write elsewhere, so it adds no wait for those loads
+// before the reads.  The DMA itself is issued outside any such function, so it
+// carries no alias metadata of its own.
+__device__ __forceinline__ int lds_read_int(const int *__restrict__ tab, int i) { return tab[i]; }
+
+// Sources of chunk c: segment seg = c*32/d of x, element offset from seg_off.
+__device__ __forceinline__ ChunkSrc chunk_src(const SrcCtx &cx, const int *seg_off, int c) {
+  ChunkSrc s;
+  const int p0 = c * kKC;
+  const int seg = p0 / cx.d;
+  const int e0 = p0 - seg * cx.d;
+  const int so = __builtin_amdgcn_readfirstlane(lds_read_int(seg_off, seg)) + e0;
+  if (seg < cx.g) {
+    s.x = cx.q0 + so;
+    s.x_valid = cx.xq_valid;
+    s.xo0 = cx.xq0;
+    s.xo1 = cx.xq1;
+  } else {
+    s.x = (seg == cx.g ? cx.k0 : cx.v0) + so;
+    s.x_valid = cx.xkv_valid;
+    s.xo0 = cx.xkv0;
+    s.xo1 = cx.xkv1;
+  }
+  s.w = cx.w1h + p0;
+  return s;
+}
+
+// Issue this wave's LDS-DMA loads of one chunk into ring slot `slot`.
+template <int WI_TOTAL>
+__device__ __forceinline__ void issue_chunk(const ChunkSrc &s, uint8_t *slot, int w_valid, int wo_base,
+                                            int w_rowstep, int wave) {
+  uint8_t *xd = slot + wave * 2 * 1024;
+  dma_1k(s.x, s.x_valid, s.xo0, xd);
+  dma_1k(s.x, s.x_valid, s.xo1, xd + 1024);
+#pragma unroll
+  for (int j = 0; j < (WI_TOTAL + 3) / 4; ++j) {
+    const int li = wave + 4 * j;  // W1 load index: rows li*16 .. li*16+15
+    if (li < WI_TOTAL) dma_1k(s.w, w_valid, wo_base + li * 16 * w_rowstep, slot + kXB + li * 1024);
+  }
+}
+
+// Accumulate K chunk `cur` into acc: Z^T[hidden block, token block] += W1 X^T.
+template <int HB>
+__device__ __forceinline__ void score_chunk(f32x16 (&acc)[(HB + 3) / 4][4], const uint8_t *__restrict__ cur,
+                                            int wave, int lrow, int half) {
+  constexpr int MBW = (HB + 3) / 4;
+  const uint8_t *ws = cur + kXB;
+#pragma unroll
+  for (int kk = 0; kk < kKC / 16; ++kk) {
+    const int lp = 2 * kk + half;
+    bf16x8 xf[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int r = tb * 32 + lrow;
+      xf[tb] = *reinterpret_cast<const bf16x8 *>(cur + r * kRowB + ((lp ^ piece_swz(r)) * 16));
+    }
+#pragma unroll
+    for (int j = 0; j < MBW; ++j) {
+      const int mb = wave + 4 * j;
+      if (mb < HB) {
+        const int r = mb * 32 + lrow;
+        const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(ws + r * kRowB + ((lp ^ piece_swz(r)) * 16));
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          acc[j][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf[tb], acc[j][tb], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int HB>  // hidden = 32 * HB
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void score_kv_kernel(const ScoreArgs a) {
+  constexpr int HS = 32 * HB;
+  constexpr int MBW = (HB + 3) / 4;          // hidden blocks per wave (blocks w, w+4, ...)
+  constexpr int WB = HS * kRowB;             // W1 chunk bytes
+  constexpr int WI_TOTAL = WB / 1024;        // 1 KB loads per W1 chunk
+  constexpr int SLOT = kXB + WB;
+  static_assert(WB % 1024 == 0, "W1 chunk split");
+
+  // One LDS object, carved by hand.  With several, the compiler tags each LDS-DMA
+  // load with its object's alias scope and then, unable to tell ring slots
+  // apart, waits for every such load before each LDS read of the ring.
+  constexpr int kOffB1 = kRing * SLOT;
+  constexpr int kOffW2 = kOffB1 + HS * 4;
+  constexpr int kOffRed = kOffW2 + HS * 4;
+  constexpr int kOffSeg = kOffRed + 4 * kTok * 4;
+  constexpr int kLds = kOffSeg + (APB_MAX_Q_HEADS + 2) * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
+  uint8_t *const ring = smem;
+  float *const sb1 = reinterpret_cast<float *>(smem + kOffB1);
+  float *const sw2 = reinterpret_cast<float *>(smem + kOffW2);
+  float(*const red)[kTok] = reinterpret_cast<float(*)[kTok]>(smem + kOffRed);
+  int *const seg_off = reinterpret_cast<int *>(smem + kOffSeg);
+
+  // Argument fields as locals.
+  const uint16_t *const q = a.q, *const k = a.k, *const v = a.v;
+  const float *const b1 = a.b1, *const w2 = a.w2, *const b2 = a.b2;
+  float *const scores = a.scores;
+  const int L = a.L, Hq = a.Hq, Hkv = a.Hkv, g = a.g, d = a.d, n_ttiles = a.n_ttiles;
 
   const int nb = gridDim.x;
   const int bid = blockIdx.x;
   const int w = (bid % kNumXcd) * (nb / kNumXcd) + bid / kNumXcd;
-  const int n_work = a.n_ttiles * a.Hkv;
-  if (w >= n_work) return;
-  const int h = w / a.n_ttiles;
-  const int tt = w - h * a.n_ttiles;
+  if (w >= n_ttiles * Hkv) return;
+  const int h = w / n_ttiles;
+  const int t0 = (w - h * n_ttiles) * kTok;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int lrow = lane & 31;
   const int half = lane >> 5;
-  const int d = a.d;
-  const int din = (a.g + 2) * d;
+  const int din = (g + 2) * d;
   const int n_chunks = din / kKC;
-  const int tok = tt * kTok + wave * 32 + lrow;
-  const bool tok_ok = tok < a.L;
+  const int valid_rows = min(L - t0, kTok);
+  const int q_row_bytes = Hq * d * 2;
+  const int kv_row_bytes = Hkv * d * 2;
   const uint16_t *w1h = a.w1 + (size_t)h * HS * din;
+  const int w_valid = HS * din * 2;
 
-  // Address of x[tok][p .. p+7] for p a multiple of 8.
-  auto x_ptr = [&](int p) -> const uint16_t * {
-    const int seg = p / d;
-    const int off = p - seg * d;
-    if (seg < a.g) return a.q + (size_t)tok * a.Hq * d + a.qhead_of_slot[h * a.g + seg] * d + off;
-    if (seg == a.g) return a.k + (size_t)tok * a.Hkv * d + h * d + off;
-    return a.v + (size_t)tok * a.Hkv * d + h * d + off;
-  };
+  for (int i = tid; i < HS; i += kThreads) {
+    sb1[i] = b1[(size_t)h * HS + i];
+    sw2[i] = w2[(size_t)h * HS + i];
+  }
+  // Element offset of each x segment inside its tensor row: q heads of the group
+  // (ascending), then k and v of head h.  The q-head table is read in place from
+  // the kernel-argument segment into its own LDS array, read once per chunk.
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint8_t *qtab = (const uint8_t *)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(ScoreArgs, qhead_of_slot);
+  for (int j = tid; j < g + 2; j += kThreads) seg_off[j] = (j < g ? (int)qtab[h * g + j] : h) * d;
+#endif
 
-  auto load_x = [&](int c, bf16x8 (&xf)[4]) {
+  // ---- per-lane DMA offsets.  Load i covers rows i*16 .. i*16+15 of a chunk;
+  // lane p writes bytes [16p, 16p+16): row i*16 + p/4, physical piece p%4.
+  const int pr = lane >> 2;
+  const int pp = lane & 3;
+  const int rx = wave * 32 + pr;  // rows of this wave's two X loads: rx and rx + 16
+  const int xq0 = rx * q_row_bytes + ((pp ^ piece_swz(rx)) * 16);
+  const int xq1 = (rx + 16) * q_row_bytes + ((pp ^ piece_swz(rx + 16)) * 16);
+  const int xkv0 = rx * kv_row_bytes + ((pp ^ piece_swz(rx)) * 16);
+  const int xkv1 = (rx + 16) * kv_row_bytes + ((pp ^ piece_swz(rx + 16)) * 16);
+  // W1 load li, lane p: row li*16 + pr; the piece swizzle depends on row bits 2..3
+  // only, which li*16 leaves unchanged.
+  const int wo_base = pr * din * 2 + ((pp ^ piece_swz(pr)) * 16);
+
+  f32x16 acc[MBW][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (tok_ok) xf[kk] = *reinterpret_cast<const bf16x8 *>(x_ptr(c * kKC + kk * 16 + half * 8));
-      else xf[kk] = bf16x8{};
-    }
-  };
-
-  uint4 wreg[WIT];
-  auto load_w = [&](int c) {
+  for (int j = 0; j < MBW; ++j)
 #pragma unroll
-    for (int it = 0; it < WIT; ++it) {
-      const int piece = it * kThreads + tid;
-      if (piece < WCH) {
-        const int row = piece / (kKC / 8);
-        const int col = piece % (kKC / 8);
-        wreg[it] = *reinterpret_cast<const uint4 *>(w1h + (size_t)row * din + c * kKC + col * 8);
-      }
-    }
-  };
-  auto store_w = [&](uint16_t *buf) {
-#pragma unroll
-    for (int it = 0; it < WIT; ++it) {
-      const int piece = it * kThreads + tid;
-      if (piece < WCH) {
-        const int row = piece / (kKC / 8);
-        const int col = piece % (kKC / 8);
-        *reinterpret_cast<uint4 *>(buf + row * kWP + col * 8) = wreg[it];
-      }
-    }
-  };
+    for (int tb = 0; tb < 4; ++tb) acc[j][tb] = f32x16{};
 
-  f32x16 acc[HSB];
-#pragma unroll
-  for (int mb = 0; mb < HSB; ++mb) acc[mb] = f32x16{};
+  __syncthreads();  // seg_off, sb1, sw2 written
 
-  bf16x8 xcur[4], xnext[4];
-  load_x(0, xcur);
-  load_w(0);
-  store_w(wbuf[0]);
-  __syncthreads();
+  const SrcCtx ctx{q + (size_t)t0 * Hq * d, k + (size_t)t0 * Hkv * d, v + (size_t)t0 * Hkv * d, w1h,
+                   valid_rows * q_row_bytes, valid_rows * kv_row_bytes, xq0, xq1, xkv0, xkv1, g, d};
 
+  // ---- prologue: chunks 0 and 1 in flight
+  issue_chunk<WI_TOTAL>(chunk_src(ctx, seg_off, 0), ring, w_valid, wo_base, din * 2, wave);
+  if (n_chunks > 1) {
+    issue_chunk<WI_TOTAL>(chunk_src(ctx, seg_off, 1), ring + SLOT, w_valid, wo_base, din * 2, wave);
+    wait_all_but_newest_chunk<WI_TOTAL>(wave);
+  } else {
+    wait_vmcnt<0>();
+  }
+  barrier_keep_dma();
+
+  // ---- main loop: chunk c in slot c % 3; chunk c+1 landed or landing; chunk c+2
+  // issued here into the third slot.
+  int slot = 0;
   for (int c = 0; c < n_chunks; ++c) {
-    if (c + 1 < n_chunks) {
-      load_x(c + 1, xnext);
-      load_w(c + 1);
-    }
-    const uint16_t *wb = wbuf[c & 1];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-      for (int mb = 0; mb < HSB; ++mb) {
-        const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(wb + (mb * 32 + lrow) * kWP + kk * 16 + half * 8);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xcur[kk], acc[mb], 0, 0, 0);
-      }
-    }
-    if (c + 1 < n_chunks) {
-      store_w(wbuf[(c + 1) & 1]);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) xcur[kk] = xnext[kk];
-    }
-    __syncthreads();
+    const bool more = c + 2 < n_chunks;
+    const int s2 = (slot + 2 >= kRing) ? slot + 2 - kRing : slot + 2;
+    if (more) issue_chunk<WI_TOTAL>(chunk_src(ctx, seg_off, c + 2), ring + s2 * SLOT, w_valid, wo_base, din * 2, wave);
+    score_chunk<HB>(acc, ring + slot * SLOT, wave, lrow, half);
+    // chunk c+1 must have landed; this wave's loads of chunk c+2 may stay in flight
+    if (more) wait_all_but_newest_chunk<WI_TOTAL>(wave);
+    else wait_vmcnt<0>();
+    barrier_keep_dma();
+    slot = (slot + 1 == kRing) ? 0 : slot + 1;
   }
 
-  // Epilogue: lane holds hidden units mb*32 + 8*(i/4) + 4*half + i%4 of token `tok`.
-  const float *b1h = a.b1 + (size_t)h * HS;
-  const float *w2h = a.w2 + (size_t)h * HS;
-  float part = 0.f;
+  // ---- epilogue: lane holds hidden units mb*32 + 8*(i/4) + 4*half + i%4 of
+  // tokens tb*32 + lrow; partial w2 . relu(z + b1) per token, then sum waves.
 #pragma unroll
-  for (int mb = 0; mb < HSB; ++mb) {
+  for (int tb = 0; tb < 4; ++tb) {
+    float part = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int u = mb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-      part = fmaf(w2h[u], fmaxf(acc[mb][i] + b1h[u], 0.f), part);
+    for (int j = 0; j < MBW; ++j) {
+      const int mb = wave + 4 * j;
+      if (mb < HB) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int u = mb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+          part = fmaf(sw2[u], fmaxf(acc[j][tb][i] + sb1[u], 0.f), part);
+        }
+      }
     }
+    part = half_swap_sum(part);
+    if (half == 0) red[wave][tb * 32 + lrow] = part;
   }
-  const float tot = half_swap_sum(part) + a.b2[h];
-  if (tok_ok && half == 0) a.scores[(size_t)h * a.L + tok] = tot;
+  __syncthreads();
+  if (tid < valid_rows) {
+    const float sc = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid] + b2[h];
+    scores[(size_t)h * L + t0 + tid] = sc;
+  }
 }
 
-template <int HSB>
+template <int HB>
 hipError_t launch_hs(ScoreArgs &a, hipStream_t s) {
   a.n_ttiles = (a.L + kTok - 1) / kTok;
   const int n_work = a.n_ttiles * a.Hkv;
   const int grid = (n_work + kNumXcd - 1) / kNumXcd * kNumXcd;
-  hipLaunchKernelGGL((score_kv_kernel<HSB>), dim3(grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((score_kv_kernel<HB>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
