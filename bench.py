@@ -11,6 +11,15 @@ the all-gather between hosts.
 Prints one JSON line.  `value` is prefill tokens/s of the host block (L / step
 time); `roofline` covers the attention kernel (HIP events around its launches);
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
+
+Two extra objects (skipped with --no-extras) time the same attention kernel
+outside the step:
+  * `split_phase`: anchor + local, then passing, then the merge of the two
+    partial results (what lets the exchange between hosts overlap compute);
+  * `modes`: the per-host attention of the two baselines the pages compare APB
+    with, at the same layer shape: Star Attention (anchor = the whole first
+    block, no passing block) and full causal FlashAttention-style attention of
+    the last host (every earlier token visible, no anchor).
 """
 from __future__ import annotations
 
@@ -76,6 +85,76 @@ def measured_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
+def _median_ms(fn, reps: int, warm: int) -> float:
+    """Median of `reps` HIP-event timings of fn() on the current stream."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def split_phase(B, pr, host, ka, va, kp, vp, attn_ms, reps=10, warm=3):
+    """Attention in two phases plus the merge, each timed alone (medians)."""
+    import torch
+    L, Hq, d = pr.local_len, pr.n_q_heads, pr.head_dim
+    o1 = torch.empty((L, Hq, d), dtype=torch.bfloat16, device="cuda")
+    o2, om = torch.empty_like(o1), torch.empty_like(o1)
+    l1 = torch.empty((Hq, L), dtype=torch.float32, device="cuda")
+    l2, lm = torch.empty_like(l1), torch.empty_like(l1)
+    seg1 = B.APB_SEG_ANCHOR | B.APB_SEG_LOCAL
+    ph1 = _median_ms(lambda: B.apb_block_attention_segments(pr, seg1, host.q, ka, va, kp, vp, host.k, host.v,
+                                                            out=o1, lse=l1), reps, warm)
+    ph2 = _median_ms(lambda: B.apb_block_attention_segments(pr, B.APB_SEG_PASSING, host.q, ka, va, kp, vp,
+                                                            host.k, host.v, out=o2, lse=l2), reps, warm)
+    mg = _median_ms(lambda: B.apb_merge_attention(pr, o1, l1, o2, l2, out=om, lse=lm), reps, warm)
+    merge_bytes = 3.0 * L * Hq * d * 2 + 3.0 * Hq * L * 4
+    return {"ms_anchor_local": ph1, "ms_passing": ph2, "ms_merge": mg, "ms_total": ph1 + ph2 + mg,
+            "ms_one_pass": attn_ms, "overhead_vs_one_pass": (ph1 + ph2 + mg) / attn_ms - 1.0,
+            "merge_gbs": merge_bytes / (mg * 1e-3) / 1e9, "merge_frac_hbm_peak":
+            merge_bytes / (mg * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+def baseline_modes(B, w, host, prior_kv, attn_ms, reps=5, warm=2):
+    """Per-host attention of Star Attention and of full causal attention, same kernel and shape."""
+    import torch
+    L, Hq, Hkv, d, p = w.local_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.host
+    out = torch.empty((L, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((Hq, L), dtype=torch.float32, device="cuda")
+    res = {}
+    # Star Attention: the anchor is the whole first block; no passing block.
+    k0, v0 = prior_kv[0]
+    pr = B.Problem(Hq, Hkv, d, L, L, 0, p, w.n_hosts, None)
+    ms = _median_ms(lambda: B.apb_block_attention(pr, host.q, k0, v0, None, None, host.k, host.v,
+                                                  out=out, lse=lse), reps, warm)
+    pairs = L * L + L * (L + 1) // 2
+    res["star"] = {"anchor_len": L, "pass_len": 0, "ms": ms, "pairs_per_head": pairs}
+    # Full causal attention of the last host: every earlier token visible, as one passing block.
+    kf = torch.cat([kv[0] for kv in prior_kv])
+    vf = torch.cat([kv[1] for kv in prior_kv])
+    pr = B.Problem(Hq, Hkv, d, L, 0, L, p, w.n_hosts, None)
+    ms = _median_ms(lambda: B.apb_block_attention(pr, host.q, None, None, kf, vf, host.k, host.v,
+                                                  out=out, lse=lse), reps, warm)
+    pairs = L * p * L + L * (L + 1) // 2
+    res["full_causal"] = {"anchor_len": 0, "pass_len": p * L, "ms": ms, "pairs_per_head": pairs}
+    del kf, vf
+    apb_pairs = L * w.anchor_len + L * w.pass_len + L * (L + 1) // 2
+    for m in res.values():
+        fl = 4.0 * d * Hq * m["pairs_per_head"]
+        m["tflops"] = fl / (m["ms"] * 1e-3) / 1e12
+        m["frac_bf16_peak"] = m["tflops"] / PEAK_BF16_TFLOPS
+        m["pairs_vs_apb"] = m["pairs_per_head"] / apb_pairs
+        m["apb_attention_speedup"] = m["ms"] / attn_ms
+    return res
+
+
 def cpu_baseline(w, blocks, weights, anchor, n_rows=4096):
     """Time the CPU oracle on a bounded sample of one host step; scale to tokens/s."""
     from oracle import apb_oracle as orc
@@ -125,6 +204,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the split-phase and baseline-mode attention timings")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before warm-up, run one plain device-to-device copy of this many MiB "
                          "(a known-size reference for HBM byte counters)")
@@ -154,6 +235,7 @@ def main():
     ka = to_device_bf16(ka_np) if w.anchor_len else None
     va = to_device_bf16(va_np) if w.anchor_len else None
     kcs, vcs = [], []
+    prior_kv = []
     host_np = None
     for j in range(w.host + 1):
         q, k, v = synth.host_block(w, j)
@@ -164,6 +246,8 @@ def main():
             _, _, kc, vc = pipeline.compress(pj, sc, ht)
             kcs.append(kc)
             vcs.append(vc)
+            if not args.no_extras:
+                prior_kv.append((ht.k, ht.v))
             del ht
         else:
             host = ht
@@ -221,7 +305,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
     }
-    del buf, host, kcs, vcs
+    if not args.no_extras and prior_kv:
+        print("# split-phase attention and baseline modes", file=sys.stderr, flush=True)
+        result["split_phase"] = split_phase(B, pr, host, ka, va, buf.k_pass, buf.v_pass, attn_ms)
+        result["modes"] = baseline_modes(B, w, host, prior_kv, attn_ms)
+    del buf, host, kcs, vcs, prior_kv
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle on a bounded sample)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, host_np, wts, (ka_np, va_np))

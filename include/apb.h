@@ -14,6 +14,9 @@
  *   apb_block_attention  attention of the local queries over
  *                        [anchor | passing | local, causal].
  *
+ * apb_block_attention_segments and apb_merge_attention compute step 4 in parts
+ * (anchor + local first, passing once it has arrived) and merge the parts.
+ *
  * The steps are described on the juejin.cn explainer of APB, sections
  * "APB 的主要功能" (main functions) and "APB 的技术原理" (technical principles),
  * and in the paper's arXiv abstract (mlsanity.com/paper/2502.12085).
@@ -22,7 +25,8 @@
  *   - Tensors are caller-owned, contiguous, row-major DEVICE buffers, token
  *     major: [rows][heads][head_dim].  bf16 tensors are passed as void*.
  *     Every tensor pointer must be 16-byte aligned.  Outputs must not alias
- *     inputs.  The library allocates no device memory and keeps no state
+ *     inputs (apb_merge_attention may write in place, see there).  The library
+ *     allocates no device memory and keeps no state
  *     between calls other than a per-process cache of device properties.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls are asynchronous on that stream, reentrant and deterministic
@@ -44,7 +48,7 @@
 extern "C" {
 #endif
 
-#define APB_ABI_VERSION 1
+#define APB_ABI_VERSION 2
 
 /* Upper limits of this implementation (APB_ERR_UNSUPPORTED beyond them). */
 #define APB_MAX_Q_HEADS 256
@@ -156,6 +160,52 @@ apb_status apb_block_attention(const apb_problem *problem, const void *q_local,
                                const void *k_pass, const void *v_pass,
                                const void *k_local, const void *v_local,
                                float softmax_scale, void *out, float *lse, void *stream);
+
+/*
+ * Key segments of step 4, for computing it in parts.  The passing block is the
+ * only input that depends on the exchange between hosts (explainer,
+ * "APB 的主要功能": the compressed blocks are all-gathered into the passing block,
+ * then each host attends over anchor, passing and local blocks), so a host can
+ * attend over anchor + local while the exchange is in flight, attend over the
+ * passing block once it has arrived, and merge the two partial results.
+ */
+#define APB_SEG_ANCHOR 1u
+#define APB_SEG_PASSING 2u
+#define APB_SEG_LOCAL 4u
+#define APB_SEG_ALL 7u
+
+/*
+ * Step 4 restricted to the key segments in `segments` (a non-zero OR of
+ * APB_SEG_*): local query row r sees the anchor rows if APB_SEG_ANCHOR is set,
+ * the passing rows if APB_SEG_PASSING is set and local rows 0..r if
+ * APB_SEG_LOCAL is set.  Arguments as for apb_block_attention; the key/value
+ * pointers of segments left out are ignored and may be NULL.  A row that sees
+ * no key at all (LOCAL left out and the selected segments empty) gets O = 0
+ * and lse = -inf, the identity of apb_merge_attention.
+ * apb_block_attention is this call with APB_SEG_ALL.
+ */
+apb_status apb_block_attention_segments(const apb_problem *problem, uint32_t segments, const void *q_local,
+                                        const void *k_anchor, const void *v_anchor,
+                                        const void *k_pass, const void *v_pass,
+                                        const void *k_local, const void *v_local,
+                                        float softmax_scale, void *out, float *lse, void *stream);
+
+/*
+ * Merge two partial attention results over disjoint key sets into the result
+ * over their union: per q head i and local row r, with m = max(lse_a, lse_b),
+ *     w_a = exp(lse_a - m),  w_b = exp(lse_b - m)
+ *     out = (w_a * out_a + w_b * out_b) / (w_a + w_b),  lse = m + ln(w_a + w_b)
+ * (softmax over a union of key sets; the same identity FlashAttention's
+ * online softmax uses between key tiles).  Rows where both lse are -inf give
+ * out = 0, lse = -inf.  Computed in fp32.
+ *   out_a, out_b  bf16 [L][Hq][d]     lse_a, lse_b  fp32 [Hq][L] (required)
+ *   out           bf16 [L][Hq][d] (output; may be out_a or out_b itself)
+ *   lse           fp32 [Hq][L] (output; may be lse_a or lse_b itself) or NULL
+ * Only n_q_heads, head_dim and local_len of `problem` are used, but the whole
+ * problem must be valid.
+ */
+apb_status apb_merge_attention(const apb_problem *problem, const void *out_a, const float *lse_a,
+                               const void *out_b, const float *lse_b, void *out, float *lse, void *stream);
 
 /* Host-only checks of a problem description; launches nothing. */
 apb_status apb_validate_problem(const apb_problem *problem);

@@ -9,7 +9,9 @@ Plain, slow numpy in float64, one step per function, in the order the pages give
   2. keep the l highest-scoring tokens per kv head and gather their K/V rows
      (the compressed context block),
   3. concatenate the compressed blocks of the preceding hosts (the passing block),
-  4. attention of the local queries over [anchor | passing | local, causal].
+  4. attention of the local queries over [anchor | passing | local, causal],
+     also over any subset of those key segments, and the merge of two partial
+     results over disjoint key sets into the result over their union.
 
 Sources (web pages on APB, "Accelerating Distributed Long-Context Inference by
 Passing Compressed Context Blocks across GPUs"):
@@ -146,30 +148,41 @@ def build_passing(k_comps, v_comps):
 # Step 4: attention of the local queries over anchor, passing and local keys.
 # explainer, "APB 的主要功能", bullet on computation (anchor + passing + local).
 # ---------------------------------------------------------------------------
+SEGMENTS_ALL = ("anchor", "passing", "local")
+
+
 def block_attention(q, k_anchor, v_anchor, k_pass, v_pass, k_local, v_local,
                     scale=None, kv_head_of_q=None, rows=None, heads=None,
-                    chunk: int = 256):
+                    chunk: int = 256, segments=SEGMENTS_ALL):
     """Masked softmax attention in float64.
 
     Local query row r of q head i (kv head h = map[i]) sees every anchor row,
-    every passing row and local rows 0..r.  Returns (O [R, nH, d], lse [nH, R])
-    for the requested rows (default all) and q heads (default all); lse is the
-    natural log of the softmax denominator including its max shift.
+    every passing row and local rows 0..r (juejin.cn APB explainer, section
+    "APB 的主要功能", computation bullet).  `segments` names the key segments
+    attended (default all three); the arrays of segments left out are ignored.
+    Returns (O [R, nH, d], lse [nH, R]) for the requested rows (default all) and
+    q heads (default all); lse is the natural log of the softmax denominator
+    including its max shift.  A row that sees no key gets O = 0, lse = -inf.
     """
     q = np.asarray(q)
     L, Hq, d = q.shape
-    Hkv = k_local.shape[1]
+    unknown = set(segments) - set(SEGMENTS_ALL)
+    if unknown or not segments:
+        raise ValueError(f"segments must be a non-empty subset of {SEGMENTS_ALL}")
+    use_l = "local" in segments
+    Hkv = (k_local if k_local is not None else (k_anchor if k_anchor is not None else k_pass)).shape[1]
     hm = _head_map(Hq, Hkv, kv_head_of_q)
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
     heads = list(range(Hq)) if heads is None else list(heads)
 
-    def seg(x):
-        return np.zeros((0, Hkv, d)) if x is None else _f64(x)
+    def seg(x, name):
+        return _f64(x) if (x is not None and name in segments) else np.zeros((0, Hkv, d))
 
-    ka, va, kp, vp = seg(k_anchor), seg(v_anchor), seg(k_pass), seg(v_pass)
-    kl, vl = _f64(k_local), _f64(v_local)
+    ka, va = seg(k_anchor, "anchor"), seg(v_anchor, "anchor")
+    kp, vp = seg(k_pass, "passing"), seg(v_pass, "passing")
+    kl, vl = seg(k_local, "local"), seg(v_local, "local")
     n_pre = ka.shape[0] + kp.shape[0]
     out = np.empty((len(rows), len(heads), d), dtype=np.float64)
     lse = np.empty((len(heads), len(rows)), dtype=np.float64)
@@ -179,7 +192,11 @@ def block_attention(q, k_anchor, v_anchor, k_pass, v_pass, k_local, v_local,
         V = np.concatenate([va[:, h], vp[:, h], vl[:, h]], axis=0)
         for c0 in range(0, len(rows), chunk):
             rr = rows[c0:c0 + chunk]
-            n_keys = n_pre + int(rr.max()) + 1
+            n_keys = n_pre + (int(rr.max()) + 1 if use_l else 0)
+            if n_keys == 0:  # nothing visible to any of these rows
+                out[c0:c0 + len(rr), hi, :] = 0.0
+                lse[hi, c0:c0 + len(rr)] = -np.inf
+                continue
             logits = scale * (_f64(q[rr, i, :]) @ K[:n_keys].T)      # [R, n_keys]
             local_col = np.arange(n_keys) - n_pre                      # local index or < 0
             visible = local_col[None, :] <= rr[:, None]
@@ -189,6 +206,31 @@ def block_attention(q, k_anchor, v_anchor, k_pass, v_pass, k_local, v_local,
             den = e.sum(axis=1, keepdims=True)
             out[c0:c0 + len(rr), hi, :] = (e @ V[:n_keys]) / den
             lse[hi, c0:c0 + len(rr)] = (m + np.log(den))[:, 0]
+    return out, lse
+
+
+def merge_attention(o_a, lse_a, o_b, lse_b):
+    """Softmax over the union of two disjoint key sets from its two parts, float64.
+
+    With partial results (o_x [R, nH, d], lse_x [nH, R]) over key sets X_a and
+    X_b: the union's denominator is exp(lse_a) + exp(lse_b), and its output is
+    the denominator-weighted mean of o_a and o_b.  Written with the max shift
+    m = max(lse_a, lse_b) so nothing overflows; rows where both sides are empty
+    (lse = -inf) give O = 0 and lse = -inf.
+    """
+    o_a, o_b = _f64(o_a), _f64(o_b)
+    lse_a, lse_b = np.asarray(lse_a, dtype=np.float64), np.asarray(lse_b, dtype=np.float64)
+    m = np.maximum(lse_a, lse_b)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    w_a = np.exp(lse_a - m_safe)                 # exp(-inf) = 0 for an empty side
+    w_b = np.exp(lse_b - m_safe)
+    den = w_a + w_b
+    nonempty = den > 0
+    den_safe = np.where(nonempty, den, 1.0)
+    c_a = (w_a / den_safe).T[:, :, None]          # [R, nH, 1]
+    c_b = (w_b / den_safe).T[:, :, None]
+    out = np.where(nonempty.T[:, :, None], c_a * o_a + c_b * o_b, 0.0)
+    lse = np.where(nonempty, m_safe + np.log(den_safe), -np.inf)
     return out, lse
 
 

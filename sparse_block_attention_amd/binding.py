@@ -25,6 +25,11 @@ APB_ERR_UNSUPPORTED = 2
 APB_ERR_HIP = 3
 APB_ERR_INTERNAL = 4
 
+APB_SEG_ANCHOR = 1
+APB_SEG_PASSING = 2
+APB_SEG_LOCAL = 4
+APB_SEG_ALL = 7
+
 
 class ApbError(RuntimeError):
     def __init__(self, status: int, func: str, detail: str):
@@ -92,6 +97,11 @@ def lib() -> ctypes.CDLL:
                                         c_void_p]
         L.apb_block_attention.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                           c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p]
+        L.apb_block_attention_segments.argtypes = [P, ctypes.c_uint32, c_void_p, c_void_p, c_void_p,
+                                                   c_void_p, c_void_p, c_void_p, c_void_p, c_float,
+                                                   c_void_p, c_void_p, c_void_p]
+        L.apb_merge_attention.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_void_p, c_void_p]
         L.apb_validate_problem.argtypes = [P]
         L.apb_status_string.argtypes = [c_int]
         L.apb_status_string.restype = c_char_p
@@ -99,7 +109,8 @@ def lib() -> ctypes.CDLL:
         L.apb_last_error.restype = c_char_p
         L.apb_abi_version.argtypes = []
         for name in ("apb_score_kv", "apb_topk_gather", "apb_build_passing", "apb_block_attention",
-                     "apb_validate_problem", "apb_abi_version"):
+                     "apb_block_attention_segments", "apb_merge_attention", "apb_validate_problem",
+                     "apb_abi_version"):
             getattr(L, name).restype = c_int
         _lib = L
     return _lib
@@ -207,6 +218,53 @@ def apb_build_passing(problem: Problem, k_comps, v_comps, k_pass=None, v_pass=No
     return k_pass, v_pass
 
 
+def _attention_outputs(problem: Problem, dev, out, lse):
+    L, Hq, d = problem.local_len, problem.n_q_heads, problem.head_dim
+    if out is None:
+        out = torch.empty((L, Hq, d), dtype=torch.bfloat16, device=dev)
+    if lse is True:
+        lse = torch.empty((Hq, L), dtype=torch.float32, device=dev)
+    elif lse is False:
+        lse = None
+    return out, lse
+
+
+def apb_block_attention_segments(problem: Problem, segments: int, q_local, k_anchor, v_anchor,
+                                 k_pass, v_pass, k_local, v_local,
+                                 softmax_scale: Optional[float] = None, out=None, lse=True,
+                                 stream=None):
+    """Attention over the key segments in `segments` (OR of APB_SEG_*; see include/apb.h).
+
+    Returns (out bf16 [L, Hq, d], lse fp32 [Hq, L] or None).  Tensors of segments
+    left out are ignored and may be None.  lse=True allocates the log-sum-exp
+    output, lse=None/False skips it, a tensor is used as is.
+    """
+    pr = problem
+    L, Hq, Hkv, d = pr.local_len, pr.n_q_heads, pr.n_kv_heads, pr.head_dim
+    use_a, use_p, use_l = (segments & APB_SEG_ANCHOR, segments & APB_SEG_PASSING,
+                           segments & APB_SEG_LOCAL)
+    A = pr.anchor_len if use_a else 0
+    P = pr.pass_len if use_p else 0
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    out, lse = _attention_outputs(pr, q_local.device, out, lse)
+
+    def seg(t, name, rows, used):
+        return _ptr(t, name, torch.bfloat16, (rows, Hkv, d)) if used else None
+
+    cp, keep = pr.to_c()
+    st = lib().apb_block_attention_segments(
+        ctypes.byref(cp), int(segments), _ptr(q_local, "q_local", torch.bfloat16, (L, Hq, d)),
+        seg(k_anchor, "k_anchor", A, A > 0), seg(v_anchor, "v_anchor", A, A > 0),
+        seg(k_pass, "k_pass", P, P > 0), seg(v_pass, "v_pass", P, P > 0),
+        seg(k_local, "k_local", L, use_l), seg(v_local, "v_local", L, use_l),
+        float(softmax_scale), _ptr(out, "out", torch.bfloat16, (L, Hq, d)),
+        _ptr(lse, "lse", torch.float32, (Hq, L)), _stream(stream))
+    del keep
+    _check(st, "apb_block_attention_segments")
+    return out, lse
+
+
 def apb_block_attention(problem: Problem, q_local, k_anchor, v_anchor, k_pass, v_pass, k_local,
                         v_local, softmax_scale: Optional[float] = None, out=None, lse=True,
                         stream=None):
@@ -219,13 +277,7 @@ def apb_block_attention(problem: Problem, q_local, k_anchor, v_anchor, k_pass, v
     Hq, Hkv, d = pr.n_q_heads, pr.n_kv_heads, pr.head_dim
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
-    dev = q_local.device
-    if out is None:
-        out = torch.empty((L, Hq, d), dtype=torch.bfloat16, device=dev)
-    if lse is True:
-        lse = torch.empty((Hq, L), dtype=torch.float32, device=dev)
-    elif lse is False:
-        lse = None
+    out, lse = _attention_outputs(pr, q_local.device, out, lse)
     cp, keep = pr.to_c()
     st = lib().apb_block_attention(
         ctypes.byref(cp), _ptr(q_local, "q_local", torch.bfloat16, (L, Hq, d)),
@@ -239,6 +291,29 @@ def apb_block_attention(problem: Problem, q_local, k_anchor, v_anchor, k_pass, v
         _ptr(lse, "lse", torch.float32, (Hq, L)), _stream(stream))
     del keep
     _check(st, "apb_block_attention")
+    return out, lse
+
+
+def apb_merge_attention(problem: Problem, out_a, lse_a, out_b, lse_b, out=None, lse=True,
+                        stream=None):
+    """Merge two partial results over disjoint key sets (see include/apb.h).
+
+    Returns (out bf16 [L, Hq, d], lse fp32 [Hq, L] or None).  `out` / `lse` may be
+    out_a / lse_a (or the b side) to merge in place.
+    """
+    pr = problem
+    L, Hq, d = pr.local_len, pr.n_q_heads, pr.head_dim
+    out, lse = _attention_outputs(pr, out_a.device, out, lse)
+    cp, keep = pr.to_c()
+    st = lib().apb_merge_attention(
+        ctypes.byref(cp), _ptr(out_a, "out_a", torch.bfloat16, (L, Hq, d)),
+        _ptr(lse_a, "lse_a", torch.float32, (Hq, L)),
+        _ptr(out_b, "out_b", torch.bfloat16, (L, Hq, d)),
+        _ptr(lse_b, "lse_b", torch.float32, (Hq, L)),
+        _ptr(out, "out", torch.bfloat16, (L, Hq, d)),
+        _ptr(lse, "lse", torch.float32, (Hq, L)), _stream(stream))
+    del keep
+    _check(st, "apb_merge_attention")
     return out, lse
 
 

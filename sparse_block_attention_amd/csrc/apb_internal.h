@@ -39,13 +39,24 @@ struct AttnArgs {
   const uint16_t *q, *ka, *va, *kp, *vp, *kl, *vl;
   uint16_t *out;
   float *lse;               // may be null
-  int L, A, P, Hq, Hkv, g;
+  int L, A, P, Hq, Hkv, g;  // A, P: rows of the anchor / passing segments attended (0 = left out)
+  int use_local;            // 1: local rows 0..r are attended; 0: local segment left out
   int n_qtiles;             // ceil(L / rows per workgroup)
   int n_work;               // n_qtiles * Hq
   float scale_log2;         // softmax scale * log2(e)
   uint8_t qhead_of_slot[256];  // slot h*g + j -> j-th q head (ascending) of kv head h
 };
 hipError_t launch_block_attention(AttnArgs &a, int head_dim, hipStream_t s);
+
+// Merge of two partial attention results over disjoint key sets.
+struct MergeArgs {
+  const uint16_t *oa, *ob;
+  const float *la, *lb;
+  uint16_t *out;
+  float *lse;               // may be null
+  int L, Hq, d;
+};
+hipError_t launch_merge_attention(const MergeArgs &a, hipStream_t s);
 
 // Scorer: per kv head, 2-layer ReLU MLP over [q of the group; k; v].
 struct ScoreArgs {

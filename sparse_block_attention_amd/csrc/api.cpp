@@ -119,16 +119,24 @@ apb_status build_passing(const apb_problem *pr, const void *const *kh, const voi
   return APB_OK;
 }
 
-apb_status block_attention(const apb_problem *pr, const void *q, const void *ka, const void *va, const void *kp,
-                           const void *vp, const void *kl, const void *vl, float scale, void *out, float *lse,
-                           void *stream) {
+apb_status block_attention(const apb_problem *pr, uint32_t segments, const void *q, const void *ka,
+                           const void *va, const void *kp, const void *vp, const void *kl, const void *vl,
+                           float scale, void *out, float *lse, void *stream) {
   APB_TRY(apb_host::check_problem(pr));
-  const long long P = (long long)pr->host_index * pr->pass_per_host;
+  if (segments == 0 || (segments & ~APB_SEG_ALL) != 0)
+    return fail(APB_ERR_INVALID_ARGUMENT, "segments = 0x%x, need a non-zero OR of APB_SEG_*", (unsigned)segments);
+  const bool use_a = (segments & APB_SEG_ANCHOR) != 0;
+  const bool use_p = (segments & APB_SEG_PASSING) != 0;
+  const bool use_l = (segments & APB_SEG_LOCAL) != 0;
+  const long long A = use_a ? pr->anchor_len : 0;
+  const long long P = use_p ? (long long)pr->host_index * pr->pass_per_host : 0;
   APB_TRY(need_ptr(q, "q_local"));
-  APB_TRY(need_ptr(kl, "k_local"));
-  APB_TRY(need_ptr(vl, "v_local"));
   APB_TRY(need_ptr(out, "out"));
-  if (pr->anchor_len > 0) {
+  if (use_l) {
+    APB_TRY(need_ptr(kl, "k_local"));
+    APB_TRY(need_ptr(vl, "v_local"));
+  }
+  if (A > 0) {
     APB_TRY(need_ptr(ka, "k_anchor"));
     APB_TRY(need_ptr(va, "v_anchor"));
   }
@@ -142,17 +150,18 @@ apb_status block_attention(const apb_problem *pr, const void *q, const void *ka,
   apb::AttnArgs a;
   memset(&a, 0, sizeof a);
   a.q = static_cast<const uint16_t *>(q);
-  a.ka = static_cast<const uint16_t *>(ka);
-  a.va = static_cast<const uint16_t *>(va);
-  a.kp = static_cast<const uint16_t *>(kp);
-  a.vp = static_cast<const uint16_t *>(vp);
-  a.kl = static_cast<const uint16_t *>(kl);
-  a.vl = static_cast<const uint16_t *>(vl);
+  a.ka = A > 0 ? static_cast<const uint16_t *>(ka) : nullptr;
+  a.va = A > 0 ? static_cast<const uint16_t *>(va) : nullptr;
+  a.kp = P > 0 ? static_cast<const uint16_t *>(kp) : nullptr;
+  a.vp = P > 0 ? static_cast<const uint16_t *>(vp) : nullptr;
+  a.kl = use_l ? static_cast<const uint16_t *>(kl) : nullptr;
+  a.vl = use_l ? static_cast<const uint16_t *>(vl) : nullptr;
   a.out = static_cast<uint16_t *>(out);
   a.lse = lse;
   a.L = pr->local_len;
-  a.A = pr->anchor_len;
+  a.A = (int)A;
   a.P = (int)P;
+  a.use_local = use_l ? 1 : 0;
   a.Hq = pr->n_q_heads;
   a.Hkv = pr->n_kv_heads;
   a.g = pr->n_q_heads / pr->n_kv_heads;
@@ -160,6 +169,28 @@ apb_status block_attention(const apb_problem *pr, const void *q, const void *ka,
   apb_host::slot_table(pr, a.qhead_of_slot);
   return hip_status(apb::launch_block_attention(a, pr->head_dim, static_cast<hipStream_t>(stream)),
                     "apb_block_attention launch");
+}
+
+apb_status merge_attention(const apb_problem *pr, const void *oa, const float *la, const void *ob, const float *lb,
+                           void *out, float *lse, void *stream) {
+  APB_TRY(apb_host::check_problem(pr));
+  APB_TRY(need_ptr(oa, "out_a"));
+  APB_TRY(need_ptr(la, "lse_a"));
+  APB_TRY(need_ptr(ob, "out_b"));
+  APB_TRY(need_ptr(lb, "lse_b"));
+  APB_TRY(need_ptr(out, "out"));
+  if (lse != nullptr && !aligned16(lse)) return fail(APB_ERR_INVALID_ARGUMENT, "lse is not 16-byte aligned");
+  apb::MergeArgs a;
+  a.oa = static_cast<const uint16_t *>(oa);
+  a.ob = static_cast<const uint16_t *>(ob);
+  a.la = la;
+  a.lb = lb;
+  a.out = static_cast<uint16_t *>(out);
+  a.lse = lse;
+  a.L = pr->local_len;
+  a.Hq = pr->n_q_heads;
+  a.d = pr->head_dim;
+  return hip_status(apb::launch_merge_attention(a, static_cast<hipStream_t>(stream)), "apb_merge_attention launch");
 }
 
 }  // namespace
@@ -192,8 +223,21 @@ apb_status apb_build_passing(const apb_problem *problem, const void *const *k_co
 apb_status apb_block_attention(const apb_problem *problem, const void *q_local, const void *k_anchor,
                                const void *v_anchor, const void *k_pass, const void *v_pass, const void *k_local,
                                const void *v_local, float softmax_scale, void *out, float *lse, void *stream) {
-  APB_GUARD(block_attention(problem, q_local, k_anchor, v_anchor, k_pass, v_pass, k_local, v_local, softmax_scale,
-                            out, lse, stream));
+  APB_GUARD(block_attention(problem, APB_SEG_ALL, q_local, k_anchor, v_anchor, k_pass, v_pass, k_local, v_local,
+                            softmax_scale, out, lse, stream));
+}
+
+apb_status apb_block_attention_segments(const apb_problem *problem, uint32_t segments, const void *q_local,
+                                        const void *k_anchor, const void *v_anchor, const void *k_pass,
+                                        const void *v_pass, const void *k_local, const void *v_local,
+                                        float softmax_scale, void *out, float *lse, void *stream) {
+  APB_GUARD(block_attention(problem, segments, q_local, k_anchor, v_anchor, k_pass, v_pass, k_local, v_local,
+                            softmax_scale, out, lse, stream));
+}
+
+apb_status apb_merge_attention(const apb_problem *problem, const void *out_a, const float *lse_a, const void *out_b,
+                               const float *lse_b, void *out, float *lse, void *stream) {
+  APB_GUARD(merge_attention(problem, out_a, lse_a, out_b, lse_b, out, lse, stream));
 }
 
 }  // extern "C"

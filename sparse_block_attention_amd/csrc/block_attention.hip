@@ -212,7 +212,7 @@ void block_attention_kernel(const AttnArgs a) {
   const int nA = (a.A + BN - 1) / BN;
   const int nP = (a.P + BN - 1) / BN;
   const int last_row = min(r0 + BM, a.L);
-  const int nL = (last_row + BN - 1) / BN;
+  const int nL = a.use_local ? (last_row + BN - 1) / BN : 0;
   const int n_tiles = nA + nP + nL;
 
   auto tile_ref = [&](int t) {
@@ -411,7 +411,8 @@ void block_attention_kernel(const AttnArgs a) {
   for (int s = 0; s < NSUB; ++s) {
     const int row = rw + s * 32 + lrow;
     const float l_tot = half_swap_sum(l_run[s]);
-    const float inv = 1.f / l_tot;
+    // l_tot == 0 only when the row saw no key at all (segments left out): O = 0, lse = -inf
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (row < a.L) {
       uint16_t *orow = a.out + row * q_stride + qhead * D;
 #pragma unroll
@@ -425,7 +426,8 @@ void block_attention_kernel(const AttnArgs a) {
         }
       }
       if (a.lse != nullptr && half == 0) {
-        a.lse[(size_t)qhead * a.L + row] = (m_run[s] + __log2f(l_tot)) * 0.69314718055994531f;
+        a.lse[(size_t)qhead * a.L + row] =
+            l_tot > 0.f ? (m_run[s] + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       }
     }
   }

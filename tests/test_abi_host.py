@@ -56,7 +56,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert B.apb_abi_version() == 1
+    assert B.apb_abi_version() == 2
     assert B.apb_status_string(B.APB_OK) == "APB_OK"
     assert B.apb_status_string(B.APB_ERR_UNSUPPORTED) == "APB_ERR_UNSUPPORTED"
     assert B.apb_status_string(99) == "APB_ERR_UNKNOWN"
@@ -117,6 +117,50 @@ def test_attention_rejects_bad_problem(lib):
     assert _call_attention(lib, _problem(n_q_heads=3)) == B.APB_ERR_INVALID_ARGUMENT
     assert lib.apb_block_attention(None, 0x1000, 0, 0, 0, 0, 0x2000, 0x3000, ctypes.c_float(1.0),
                                    0x4000, None, None) == B.APB_ERR_INVALID_ARGUMENT
+
+
+def _call_segments(lib, pr, segments, q=0x1000, ka=0x2000, va=0x3000, kp=0x4000, vp=0x5000, kl=0x6000,
+                   vl=0x7000, scale=0.125, out=0x8000, lse=None):
+    cp, keep = pr.to_c()
+    return lib.apb_block_attention_segments(ctypes.byref(cp), segments, q, ka, va, kp, vp, kl, vl,
+                                            ctypes.c_float(scale), out, lse, None)
+
+
+@pytest.mark.parametrize("segments,override,code,needle", [
+    (0, {}, B.APB_ERR_INVALID_ARGUMENT, "segments"),
+    (8, {}, B.APB_ERR_INVALID_ARGUMENT, "segments"),
+    (B.APB_SEG_ALL | 16, {}, B.APB_ERR_INVALID_ARGUMENT, "segments"),
+    (B.APB_SEG_LOCAL, {"kl": None}, B.APB_ERR_INVALID_ARGUMENT, "k_local"),
+    (B.APB_SEG_ANCHOR, {"va": 0x3008}, B.APB_ERR_INVALID_ARGUMENT, "v_anchor"),
+    (B.APB_SEG_PASSING, {"kp": None}, B.APB_ERR_INVALID_ARGUMENT, "k_pass"),
+    # segments left out: their pointers are not looked at (the bad q still stops the call)
+    (B.APB_SEG_PASSING, {"ka": None, "kl": None, "vl": 0x7001, "q": None}, B.APB_ERR_INVALID_ARGUMENT,
+     "q_local"),
+    (B.APB_SEG_ANCHOR | B.APB_SEG_LOCAL, {"kp": None, "vp": None, "out": None}, B.APB_ERR_INVALID_ARGUMENT,
+     "out"),
+    (B.APB_SEG_ALL, {"scale": -1.0}, B.APB_ERR_INVALID_ARGUMENT, "softmax_scale"),
+])
+def test_segment_attention_rejects_bad_arguments(lib, segments, override, code, needle):
+    st = _call_segments(lib, _problem(), segments, **override)
+    assert st == code
+    assert needle in B.apb_last_error()
+
+
+def test_merge_rejects_bad_arguments(lib):
+    cp, keep = _problem().to_c()
+    good = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000]
+    names = ["out_a", "lse_a", "out_b", "lse_b", "out"]
+    for i, name in enumerate(names):
+        for bad in (None, good[i] + 4):
+            args = list(good)
+            args[i] = bad
+            assert lib.apb_merge_attention(ctypes.byref(cp), *args, None) == B.APB_ERR_INVALID_ARGUMENT
+            assert name in B.apb_last_error()
+    args = list(good[:5]) + [0x6004]
+    assert lib.apb_merge_attention(ctypes.byref(cp), *args, None) == B.APB_ERR_INVALID_ARGUMENT
+    assert "lse" in B.apb_last_error()
+    cp, keep = _problem(head_dim=96).to_c()
+    assert lib.apb_merge_attention(ctypes.byref(cp), *good, None) == B.APB_ERR_UNSUPPORTED
 
 
 def test_score_rejects_bad_scorer(lib):

@@ -168,6 +168,97 @@ def test_row_subset_matches_all_rows():
     np.testing.assert_allclose(lse2[0], lse[1, rows], rtol=1e-13)
 
 
+# ------------------------------------------------------------- attention in parts + merge
+
+
+def _sdpa_masked(q, K, V, visible, head_map, scale):
+    """torch SDPA (float64) of q [R, Hq, d] over keys K, V [n, Hkv, d] with a boolean
+    visibility mask [R, n]; also the log-sum-exp from torch.logsumexp."""
+    R, Hq, d = q.shape
+    kx = np.stack([K[:, head_map[i], :] for i in range(Hq)], axis=0)[None]   # [1, Hq, n, d]
+    vx = np.stack([V[:, head_map[i], :] for i in range(Hq)], axis=0)[None]
+    tq = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))[None]
+    tk, tv = torch.from_numpy(kx), torch.from_numpy(vx)
+    mask = torch.from_numpy(visible)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+    logits = torch.matmul(tq, tk.transpose(-1, -2)) * scale
+    lse = torch.logsumexp(logits.masked_fill(~mask, float("-inf")), dim=-1)
+    return o[0].numpy().transpose(1, 0, 2), lse[0].numpy()
+
+
+def _parts_problem(seed=60, A=6, P=10, L=13, Hq=4, Hkv=2, d=8):
+    r = lambda shape, s: _rand(shape, seed + s)
+    return (r((L, Hq, d), 0), r((A, Hkv, d), 1), r((A, Hkv, d), 2), r((P, Hkv, d), 3),
+            r((P, Hkv, d), 4), r((L, Hkv, d), 5), r((L, Hkv, d), 6))
+
+
+SEGMENT_SUBSETS = [s for n in (1, 2, 3) for s in itertools.combinations(orc.SEGMENTS_ALL, n)]
+
+
+@pytest.mark.parametrize("segments", SEGMENT_SUBSETS, ids=lambda s: "+".join(s))
+def test_segment_subset_equals_masked_sdpa(segments):
+    """Any subset of the key segments: SDPA over the chosen keys, the local ones causal."""
+    q, ka, va, kp, vp, kl, vl = _parts_problem()
+    hm = np.array([1, 0, 0, 1])
+    L = q.shape[0]
+    Ks, Vs, vis = [], [], []
+    for name, K, V in (("anchor", ka, va), ("passing", kp, vp)):
+        if name in segments:
+            Ks.append(K)
+            Vs.append(V)
+            vis.append(np.ones((L, K.shape[0]), dtype=bool))
+    if "local" in segments:
+        Ks.append(kl)
+        Vs.append(vl)
+        vis.append(np.tril(np.ones((L, L), dtype=bool)))
+    o_ref, lse_ref = _sdpa_masked(q, np.concatenate(Ks), np.concatenate(Vs), np.concatenate(vis, axis=1),
+                                  hm, 0.4)
+    o, lse = orc.block_attention(q, ka, va, kp, vp, kl, vl, scale=0.4, kv_head_of_q=hm,
+                                 segments=segments, chunk=5)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("split", [(("anchor", "local"), ("passing",)),
+                                   (("anchor",), ("passing", "local")),
+                                   (("local",), ("anchor", "passing"))],
+                         ids=["al|p", "a|pl", "l|ap"])
+def test_merge_of_two_parts_equals_whole(split):
+    """Softmax over a disjoint union: merging the parts gives the one-pass result."""
+    q, ka, va, kp, vp, kl, vl = _parts_problem(seed=70)
+    o_all, lse_all = orc.block_attention(q, ka, va, kp, vp, kl, vl)
+    oa, la = orc.block_attention(q, ka, va, kp, vp, kl, vl, segments=split[0])
+    ob, lb = orc.block_attention(q, ka, va, kp, vp, kl, vl, segments=split[1])
+    o, lse = orc.merge_attention(oa, la, ob, lb)
+    np.testing.assert_allclose(o, o_all, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_all, rtol=1e-13, atol=1e-13)
+    o2, lse2 = orc.merge_attention(ob, lb, oa, la)           # symmetric
+    np.testing.assert_allclose(o2, o, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-15)
+
+
+def test_merge_closed_forms():
+    """Empty side (lse = -inf) is the identity; a part merged with itself keeps O and
+    adds ln 2 to lse; two empty sides stay empty (O = 0, lse = -inf)."""
+    o = _rand((5, 3, 4), 80)
+    lse = _rand((3, 5), 81)
+    empty_o, empty_l = np.full_like(o, 7.0), np.full_like(lse, -np.inf)
+    m, ml = orc.merge_attention(o, lse, empty_o, empty_l)
+    assert np.array_equal(m, o) and np.array_equal(ml, lse)
+    m, ml = orc.merge_attention(o, lse, o, lse)
+    np.testing.assert_allclose(m, o, rtol=1e-15)
+    np.testing.assert_allclose(ml, lse + np.log(2.0), rtol=1e-15, atol=1e-15)
+    m, ml = orc.merge_attention(empty_o, empty_l, empty_o, empty_l)
+    assert np.all(m == 0.0) and np.all(ml == -np.inf)
+
+
+def test_rows_with_no_visible_key():
+    """Passing only with P = 0: nothing to attend, O = 0 and lse = -inf."""
+    q, ka, va, kp, vp, kl, vl = _parts_problem(P=0)
+    o, lse = orc.block_attention(q, ka, va, kp, vp, kl, vl, segments=("passing",))
+    assert np.all(o == 0.0) and np.all(lse == -np.inf)
+
+
 # --------------------------------------------------------------------------- scorer
 
 
