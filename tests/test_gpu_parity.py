@@ -144,6 +144,7 @@ def test_attention_segment_edges(L, A, p, l, Hq, Hkv, d):
 @pytest.mark.parametrize("L,l,specials", [
     (1, 1, True), (7, 3, True), (256, 85, True), (16384, 1024, True), (16385, 5000, True),
     (16384, 16384, False), (131072, 4096, True), (3000, 2999, False),
+    (32768, 2048, True), (32769, 100, True), (25600, 1600, False),
 ])
 def test_topk_gather_ties_and_specials(L, l, specials):
     """Bit-exact selection on tie-heavy scores with -inf/+inf/-0/+0/NaN, LDS and global paths."""
@@ -151,6 +152,26 @@ def test_topk_gather_ties_and_specials(L, l, specials):
     s = synth.tie_heavy_scores(Hkv, L, seed=L + l, specials=specials)
     k = synth.random_bf16((L, Hkv, d), 8, stream=L)
     v = synth.random_bf16((L, Hkv, d), 9, stream=L)
+    pr = B.Problem(Hkv, Hkv, d, L, 0, l, 1, 2, None)
+    idx, kc, vc = B.apb_topk_gather(pr, to_device_f32(s), to_device_bf16(k), to_device_bf16(v))
+    torch.cuda.synchronize()
+    idx_np = _np(idx)
+    assert np.array_equal(idx_np, orc.topl(s, l))
+    kr, vr = orc.gather(k, v, idx_np)
+    assert np.array_equal(from_device_bf16(kc), kr) and np.array_equal(from_device_bf16(vc), vr)
+
+
+@pytest.mark.parametrize("L,l,spread", [(5000, 700, 600), (16384, 1024, 1 << 13), (40000, 4096, 1 << 21)])
+def test_topk_gather_near_equal_scores(L, l, spread):
+    """Scores a few ulps apart (random bit patterns above 1.0 and below -1.0, ties included):
+    the low radix digits decide, across the 12/12/8-bit digit boundaries."""
+    Hkv, d = 2, 128
+    rng = np.random.default_rng(L + spread)
+    bits = (0x3F800000 + rng.integers(0, spread, size=(Hkv, L))).astype(np.uint32)
+    bits[:, ::3] |= np.uint32(0x80000000)                      # every third one negative
+    s = bits.view(np.float32)
+    k = synth.random_bf16((L, Hkv, d), 12, stream=L)
+    v = synth.random_bf16((L, Hkv, d), 13, stream=L)
     pr = B.Problem(Hkv, Hkv, d, L, 0, l, 1, 2, None)
     idx, kc, vc = B.apb_topk_gather(pr, to_device_f32(s), to_device_bf16(k), to_device_bf16(v))
     torch.cuda.synchronize()
