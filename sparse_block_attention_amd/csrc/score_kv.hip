@@ -7,18 +7,20 @@
 //   x = [q[t, G_h[0]]; ...; q[t, G_h[g-1]]; k[t, h]; v[t, h]]
 //   s = w2[h] . relu(W1[h] x + b1[h]) + b2[h]
 //
-// gfx950 design: a workgroup takes 128 tokens of one kv head and all Hs hidden
-// units: Z^T = W1 X^T on v_mfma_f32_32x32x16_bf16 (M = hidden, N = tokens,
-// K = (g+2)d), K walked in 32-wide chunks.  Each of the 4 waves owns a quarter
-// of the hidden blocks for all 128 tokens, so a W1 element is read from LDS by
-// one wave only.  X and W1 chunks reach LDS by LDS-DMA (buffer_load ... lds)
-// through a 3-deep ring: two chunks are in flight while one is consumed, and
-// two workgroups share a CU, which keeps enough HBM reads outstanding.  Rows of
-// a chunk are 64 bytes; their 16-byte pieces are XOR-swizzled by row so the
-// MFMA operand reads are free of bank conflicts.  The epilogue adds b1, applies
-// ReLU and the w2 dot product in fp32, and sums the four waves' partial dot
-// products through LDS.  Work items are grouped by kv head onto XCDs so a
-// head's W1 stays in one L2.
+// gfx950 design: a workgroup takes 128*TH tokens of one kv head and all Hs
+// hidden units: Z^T = W1 X^T on v_mfma_f32_32x32x16_bf16 (M = hidden, N =
+// tokens, K = (g+2)d), K walked in 32-wide chunks.  4*TH waves: wave w owns
+// hidden quarter w%4 (blocks w%4, w%4 + 4, ...) for token half w/4 (128 tokens),
+// so a W1 element is read from LDS by TH waves.  X and W1 chunks reach LDS by
+// LDS-DMA (buffer_load ... lds) through a 3-deep ring: two chunks are in flight
+// while one is consumed.  Every workgroup streams its head's whole W1 from L2,
+// so TH = 2 (256 tokens, one workgroup per CU) halves that L2 traffic against
+// TH = 1 (128 tokens, two workgroups per CU).  Rows of a chunk are 64 bytes;
+// their 16-byte pieces are XOR-swizzled by row so the MFMA operand reads are
+// free of bank conflicts.  The epilogue adds b1, applies ReLU and the w2 dot
+// product in fp32, and sums the four hidden quarters' partial dot products
+// through LDS.  Work items are grouped by kv head onto XCDs so a head's W1
+// stays in one L2.
 #include <stddef.h>
 
 #include "apb_internal.h"
@@ -26,12 +28,24 @@
 namespace apb {
 namespace {
 
-constexpr int kThreads = 256;      // 4 waves
-constexpr int kTok = 128;          // tokens per workgroup
+#ifndef APB_SCORE_TH
+#define APB_SCORE_TH 2
+#endif
+constexpr int kTH = APB_SCORE_TH;  // token halves (of 128 tokens) per workgroup
 constexpr int kKC = 32;            // K chunk (elements of x)
-constexpr int kRing = 3;           // LDS ring depth (chunks in flight: kRing - 1)
+#ifndef APB_SCORE_RING
+#define APB_SCORE_RING 3
+#endif
+constexpr int kRing = APB_SCORE_RING;  // LDS ring depth (chunks in flight: kRing - 1)
 constexpr int kRowB = kKC * 2;     // bytes per chunk row (64)
-constexpr int kXB = kTok * kRowB;  // X chunk bytes (8 KB)
+
+template <int TH>
+struct ScoreCfg {
+  static constexpr int kWaves = 4 * TH;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kTok = 128 * TH;          // tokens per workgroup
+  static constexpr int kXB = kTok * kRowB;       // X chunk bytes
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -57,21 +71,25 @@ __device__ __forceinline__ void dma_1k(const void *base, int valid_bytes, int vo
 #endif
 }
 
-// A wave issues 2 X loads plus W1 loads wave, wave+4, ... < WI_TOTAL per chunk;
-// wait until only the newest chunk's loads may be outstanding.
-template <int WI_TOTAL>
-__device__ __forceinline__ void wait_all_but_newest_chunk(int wave) {
-  if constexpr (WI_TOTAL % 4 == 0) {
-    wait_vmcnt<2 + WI_TOTAL / 4>();
-  } else {
-    switch ((WI_TOTAL - wave + 3) / 4) {
-      case 0: wait_vmcnt<2>(); break;
-      case 1: wait_vmcnt<3>(); break;
-      case 2: wait_vmcnt<4>(); break;
-      case 3: wait_vmcnt<5>(); break;
-      default: wait_vmcnt<6>(); break;
-    }
+// s_waitcnt vmcnt(n) for a wave-uniform n known only at run time (n <= 23;
+// larger n waits for everything, which is always safe).
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+#define APB_CASE(N) \
+  case N: wait_vmcnt<N>(); break;
+    APB_CASE(1) APB_CASE(2) APB_CASE(3) APB_CASE(4) APB_CASE(5) APB_CASE(6) APB_CASE(7) APB_CASE(8)
+    APB_CASE(9) APB_CASE(10) APB_CASE(11) APB_CASE(12) APB_CASE(13) APB_CASE(14) APB_CASE(15)
+    APB_CASE(16) APB_CASE(17) APB_CASE(18) APB_CASE(19) APB_CASE(20) APB_CASE(21) APB_CASE(22)
+    APB_CASE(23)
+#undef APB_CASE
+    default: wait_vmcnt<0>(); break;
   }
+}
+
+// LDS-DMA loads one wave issues per chunk: 2 of X plus W1 loads wave, wave+NW, ...
+template <int WI_TOTAL, int NW>
+__device__ __forceinline__ int loads_per_chunk(int wave) {
+  return 2 + (WI_TOTAL > wave ? (WI_TOTAL - wave + NW - 1) / NW : 0);
 }
 
 // Where chunk c comes from.
@@ -120,38 +138,40 @@ __device__ __forceinline__ ChunkSrc chunk_src(const SrcCtx &cx, const int *seg_o
   return s;
 }
 
-// Issue this wave's LDS-DMA loads of one chunk into ring slot `slot`.
-template <int WI_TOTAL>
+// Issue this wave's LDS-DMA loads of one chunk into ring slot `slot`: X rows
+// wave*32 .. wave*32+31, and W1 loads wave, wave+NW, ...
+template <int WI_TOTAL, int NW, int XB>
 __device__ __forceinline__ void issue_chunk(const ChunkSrc &s, uint8_t *slot, int w_valid, int wo_base,
                                             int w_rowstep, int wave) {
   uint8_t *xd = slot + wave * 2 * 1024;
   dma_1k(s.x, s.x_valid, s.xo0, xd);
   dma_1k(s.x, s.x_valid, s.xo1, xd + 1024);
 #pragma unroll
-  for (int j = 0; j < (WI_TOTAL + 3) / 4; ++j) {
-    const int li = wave + 4 * j;  // W1 load index: rows li*16 .. li*16+15
-    if (li < WI_TOTAL) dma_1k(s.w, w_valid, wo_base + li * 16 * w_rowstep, slot + kXB + li * 1024);
+  for (int j = 0; j < (WI_TOTAL + NW - 1) / NW; ++j) {
+    const int li = wave + NW * j;  // W1 load index: rows li*16 .. li*16+15
+    if (li < WI_TOTAL) dma_1k(s.w, w_valid, wo_base + li * 16 * w_rowstep, slot + XB + li * 1024);
   }
 }
 
-// Accumulate K chunk `cur` into acc: Z^T[hidden block, token block] += W1 X^T.
-template <int HB>
+// Accumulate K chunk `cur` into acc: Z^T[hidden block, token block] += W1 X^T,
+// for hidden quarter hq and token half th.
+template <int HB, int XB>
 __device__ __forceinline__ void score_chunk(f32x16 (&acc)[(HB + 3) / 4][4], const uint8_t *__restrict__ cur,
-                                            int wave, int lrow, int half) {
+                                            int hq, int th, int lrow, int half) {
   constexpr int MBW = (HB + 3) / 4;
-  const uint8_t *ws = cur + kXB;
+  const uint8_t *ws = cur + XB;
 #pragma unroll
   for (int kk = 0; kk < kKC / 16; ++kk) {
     const int lp = 2 * kk + half;
     bf16x8 xf[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      const int r = tb * 32 + lrow;
+      const int r = (th * 4 + tb) * 32 + lrow;
       xf[tb] = *reinterpret_cast<const bf16x8 *>(cur + r * kRowB + ((lp ^ piece_swz(r)) * 16));
     }
 #pragma unroll
     for (int j = 0; j < MBW; ++j) {
-      const int mb = wave + 4 * j;
+      const int mb = hq + 4 * j;
       if (mb < HB) {
         const int r = mb * 32 + lrow;
         const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(ws + r * kRowB + ((lp ^ piece_swz(r)) * 16));
@@ -163,11 +183,13 @@ __device__ __forceinline__ void score_chunk(f32x16 (&acc)[(HB + 3) / 4][4], cons
   }
 }
 
-template <int HB>  // hidden = 32 * HB
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+template <int HB, int TH>  // hidden = 32 * HB; 128 * TH tokens per workgroup
+__global__ __launch_bounds__(ScoreCfg<TH>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void score_kv_kernel(const ScoreArgs a) {
+  using C = ScoreCfg<TH>;
+  constexpr int kThreads = C::kThreads, kTok = C::kTok, kXB = C::kXB, NW = C::kWaves;
   constexpr int HS = 32 * HB;
-  constexpr int MBW = (HB + 3) / 4;          // hidden blocks per wave (blocks w, w+4, ...)
+  constexpr int MBW = (HB + 3) / 4;          // hidden blocks per wave (blocks hq, hq+4, ...)
   constexpr int WB = HS * kRowB;             // W1 chunk bytes
   constexpr int WI_TOTAL = WB / 1024;        // 1 KB loads per W1 chunk
   constexpr int SLOT = kXB + WB;
@@ -203,6 +225,8 @@ void score_kv_kernel(const ScoreArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int hq = wave & 3;   // hidden quarter
+  const int th = wave >> 2;  // token half
   const int lane = tid & 63;
   const int lrow = lane & 31;
   const int half = lane >> 5;
@@ -250,39 +274,46 @@ void score_kv_kernel(const ScoreArgs a) {
   const SrcCtx ctx{q + (size_t)t0 * Hq * d, k + (size_t)t0 * Hkv * d, v + (size_t)t0 * Hkv * d, w1h,
                    valid_rows * q_row_bytes, valid_rows * kv_row_bytes, xq0, xq1, xkv0, xkv1, g, d};
 
-  // ---- prologue: chunks 0 and 1 in flight
-  issue_chunk<WI_TOTAL>(chunk_src(ctx, seg_off, 0), ring, w_valid, wo_base, din * 2, wave);
-  if (n_chunks > 1) {
-    issue_chunk<WI_TOTAL>(chunk_src(ctx, seg_off, 1), ring + SLOT, w_valid, wo_base, din * 2, wave);
-    wait_all_but_newest_chunk<WI_TOTAL>(wave);
-  } else {
-    wait_vmcnt<0>();
-  }
+  // ---- prologue: chunks 0 .. PF-1 in flight (PF = kRing - 1), chunk 0 landed
+  constexpr int PF = kRing - 1;
+  const int per_chunk = loads_per_chunk<WI_TOTAL, NW>(wave);
+  const int n_pro = min(PF, n_chunks);
+  for (int c = 0; c < n_pro; ++c)
+    issue_chunk<WI_TOTAL, NW, kXB>(chunk_src(ctx, seg_off, c), ring + c * SLOT, w_valid, wo_base, din * 2, wave);
+  wait_vmcnt_dyn((n_pro - 1) * per_chunk);
   barrier_keep_dma();
 
-  // ---- main loop: chunk c in slot c % 3; chunk c+1 landed or landing; chunk c+2
-  // issued here into the third slot.
+  // ---- main loop: chunk c in slot c % kRing; chunks c+1 .. c+PF-1 landed or
+  // landing; chunk c+PF issued here into the slot chunk c-1 has freed.
   int slot = 0;
   for (int c = 0; c < n_chunks; ++c) {
-    const bool more = c + 2 < n_chunks;
-    const int s2 = (slot + 2 >= kRing) ? slot + 2 - kRing : slot + 2;
-    if (more) issue_chunk<WI_TOTAL>(chunk_src(ctx, seg_off, c + 2), ring + s2 * SLOT, w_valid, wo_base, din * 2, wave);
-    score_chunk<HB>(acc, ring + slot * SLOT, wave, lrow, half);
-    // chunk c+1 must have landed; this wave's loads of chunk c+2 may stay in flight
-    if (more) wait_all_but_newest_chunk<WI_TOTAL>(wave);
-    else wait_vmcnt<0>();
+    if (c + PF < n_chunks) {
+      const int sp = (slot + PF >= kRing) ? slot + PF - kRing : slot + PF;
+      issue_chunk<WI_TOTAL, NW, kXB>(chunk_src(ctx, seg_off, c + PF), ring + sp * SLOT, w_valid, wo_base, din * 2,
+                                     wave);
+    }
+    score_chunk<HB, kXB>(acc, ring + slot * SLOT, hq, th, lrow, half);
+    // chunk c+1 must have landed; this wave's loads of chunks c+2 .. c+PF may stay in flight
+    const int newer = min(PF, n_chunks - 1 - c) - 1;  // issued chunks after c+1
+    if constexpr (WI_TOTAL % NW == 0) {
+      if (newer == PF - 1) wait_vmcnt<(PF - 1) * (2 + WI_TOTAL / NW)>();  // steady state
+      else wait_vmcnt_dyn(newer > 0 ? newer * per_chunk : 0);
+    } else {
+      wait_vmcnt_dyn(newer > 0 ? newer * per_chunk : 0);
+    }
     barrier_keep_dma();
     slot = (slot + 1 == kRing) ? 0 : slot + 1;
   }
 
   // ---- epilogue: lane holds hidden units mb*32 + 8*(i/4) + 4*half + i%4 of
-  // tokens tb*32 + lrow; partial w2 . relu(z + b1) per token, then sum waves.
+  // tokens (th*4 + tb)*32 + lrow; partial w2 . relu(z + b1) per token, then
+  // sum the four hidden quarters.
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     float part = 0.f;
 #pragma unroll
     for (int j = 0; j < MBW; ++j) {
-      const int mb = wave + 4 * j;
+      const int mb = hq + 4 * j;
       if (mb < HB) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -292,7 +323,7 @@ void score_kv_kernel(const ScoreArgs a) {
       }
     }
     part = half_swap_sum(part);
-    if (half == 0) red[wave][tb * 32 + lrow] = part;
+    if (half == 0) red[hq][(th * 4 + tb) * 32 + lrow] = part;
   }
   __syncthreads();
   if (tid < valid_rows) {
@@ -303,10 +334,11 @@ void score_kv_kernel(const ScoreArgs a) {
 
 template <int HB>
 hipError_t launch_hs(ScoreArgs &a, hipStream_t s) {
-  a.n_ttiles = (a.L + kTok - 1) / kTok;
+  using C = ScoreCfg<kTH>;
+  a.n_ttiles = (a.L + C::kTok - 1) / C::kTok;
   const int n_work = a.n_ttiles * a.Hkv;
   const int grid = (n_work + kNumXcd - 1) / kNumXcd * kNumXcd;
-  hipLaunchKernelGGL((score_kv_kernel<HB>), dim3(grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((score_kv_kernel<HB, kTH>), dim3(grid), dim3(C::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
