@@ -4,7 +4,9 @@ One step = one host's share of one layer: score (apb_score_kv), top-l + gather
 (apb_topk_gather), passing block (apb_build_passing) and attention
 (apb_block_attention), on synthetic inputs already resident in HBM.  The
 compressed blocks of the earlier hosts are produced before timing, in place of
-the all-gather between hosts.
+the all-gather between hosts.  The host's own compression feeds later hosts,
+not its own attention, so it runs on a second stream beside the passing build
+and the attention (--serial puts everything on one stream).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
 
@@ -204,6 +206,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serial", action="store_true",
+                    help="run the host's compression on the same stream as its attention "
+                         "instead of a second stream")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the split-phase and baseline-mode attention timings")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -255,6 +260,9 @@ def main():
     torch.cuda.synchronize()
     buf = pipeline.StepBuffers.allocate(pr)
     stream = torch.cuda.current_stream()
+    # The host's own compression is independent of its attention: a second stream
+    # (default priority) lets the two overlap.
+    side = None if args.serial else torch.cuda.Stream()
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib * (1 << 20)
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -265,7 +273,7 @@ def main():
         del src, dst
     print("# warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        pipeline.host_step(pr, sc, host, ka, va, kcs, vcs, buf, stream=stream)
+        pipeline.host_step(pr, sc, host, ka, va, kcs, vcs, buf, stream=stream, side_stream=side)
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -274,7 +282,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        pipeline.host_step(pr, sc, host, ka, va, kcs, vcs, buf, stream=stream, attn_events=ev[i])
+        pipeline.host_step(pr, sc, host, ka, va, kcs, vcs, buf, stream=stream, attn_events=ev[i],
+                           side_stream=side)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps

@@ -70,19 +70,32 @@ class StepBuffers:
 
 def host_step(problem: B.Problem, scorer: dict, host: HostTensors, k_anchor, v_anchor,
               k_comps: List[torch.Tensor], v_comps: List[torch.Tensor], buf: StepBuffers,
-              softmax_scale=None, stream=None, attn_events=None) -> StepBuffers:
+              softmax_scale=None, stream=None, attn_events=None, side_stream=None) -> StepBuffers:
     """The whole per-host path into `buf`.  `attn_events` = (start, end) HIP events
-    recorded around the attention launch on the same stream, or None."""
-    B.apb_score_kv(problem, scorer, host.q, host.k, host.v, scores=buf.scores, stream=stream)
+    recorded around the attention launch on the same stream, or None.
+
+    The host's own compression (score, top-l, gather) feeds the later hosts, not
+    this host's attention, so with `side_stream` it runs there, concurrently with
+    the passing build and the attention on `stream`; the call returns with
+    `stream` made to wait for it, so the whole step is ordered before anything
+    enqueued on `stream` afterwards.  Both streams keep the default priority.
+    """
+    main = stream if stream is not None else torch.cuda.current_stream()
+    comp = side_stream if side_stream is not None else main
+    if side_stream is not None:
+        side_stream.wait_stream(main)          # inputs of this step are ready
+    B.apb_score_kv(problem, scorer, host.q, host.k, host.v, scores=buf.scores, stream=comp)
     B.apb_topk_gather(problem, buf.scores, host.k, host.v, idx=buf.idx, k_comp=buf.k_comp,
-                      v_comp=buf.v_comp, stream=stream)
+                      v_comp=buf.v_comp, stream=comp)
     if problem.pass_len:
         B.apb_build_passing(problem, k_comps, v_comps, k_pass=buf.k_pass, v_pass=buf.v_pass,
-                            stream=stream)
+                            stream=main)
     if attn_events is not None:
-        attn_events[0].record(stream)
+        attn_events[0].record(main)
     B.apb_block_attention(problem, host.q, k_anchor, v_anchor, buf.k_pass, buf.v_pass, host.k,
-                          host.v, softmax_scale, out=buf.out, lse=buf.lse, stream=stream)
+                          host.v, softmax_scale, out=buf.out, lse=buf.lse, stream=main)
     if attn_events is not None:
-        attn_events[1].record(stream)
+        attn_events[1].record(main)
+    if side_stream is not None:
+        main.wait_stream(side_stream)          # the step ends when both halves have
     return buf

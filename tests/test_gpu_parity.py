@@ -181,6 +181,31 @@ def test_topk_gather_near_equal_scores(L, l, spread):
     assert np.array_equal(from_device_bf16(kc), kr) and np.array_equal(from_device_bf16(vc), vr)
 
 
+def test_host_step_on_two_streams_matches_one_stream():
+    """Compression on a side stream beside the attention: identical bits to one stream."""
+    w = synth.Workload("two_streams", 208, 3, 300, 40, 50, 4, 2, 128, 64, 1.0, 2)
+    wts = synth.scorer_weights(w)
+    sc = _dev_scorer(wts)
+    ka, va = (to_device_bf16(x) for x in synth.anchor_kv(w))
+    comps = []
+    for j in range(w.host):
+        q, k, v = synth.host_block(w, j)
+        ht = pipeline.HostTensors(to_device_bf16(q), to_device_bf16(k), to_device_bf16(v))
+        comps.append(pipeline.compress(_problem(w, j), sc, ht)[2:])
+    q, k, v = synth.host_block(w, w.host)
+    host = pipeline.HostTensors(to_device_bf16(q), to_device_bf16(k), to_device_bf16(v))
+    pr = _problem(w)
+    kcs, vcs = [c[0] for c in comps], [c[1] for c in comps]
+    one = pipeline.host_step(pr, sc, host, ka, va, kcs, vcs, pipeline.StepBuffers.allocate(pr))
+    side = torch.cuda.Stream()
+    buf = pipeline.StepBuffers.allocate(pr)
+    for _ in range(3):
+        two = pipeline.host_step(pr, sc, host, ka, va, kcs, vcs, buf, side_stream=side)
+    torch.cuda.synchronize()
+    for name in ("scores", "idx", "k_comp", "v_comp", "k_pass", "v_pass", "out", "lse"):
+        assert torch.equal(getattr(one, name), getattr(two, name)), name
+
+
 def test_build_passing_many_hosts():
     """p = 130 earlier hosts: more than one launch of the batched copy."""
     p, l, Hkv, d = 130, 3, 2, 64
