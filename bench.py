@@ -21,7 +21,9 @@ outside the step:
   * `modes`: the per-host attention of the two baselines the pages compare APB
     with, at the same layer shape: Star Attention (anchor = the whole first
     block, no passing block) and full causal FlashAttention-style attention of
-    the last host (every earlier token visible, no anchor).
+    the last host (every earlier token visible, no anchor);
+  * `layer_sides`: rotary embedding of the host's q and k, and the anchor's
+    own causal attention (steps either side of the attention step).
 """
 from __future__ import annotations
 
@@ -154,6 +156,29 @@ def baseline_modes(B, w, host, prior_kv, attn_ms, reps=5, warm=2):
         m["frac_bf16_peak"] = m["tflops"] / PEAK_BF16_TFLOPS
         m["pairs_vs_apb"] = m["pairs_per_head"] / apb_pairs
         m["apb_attention_speedup"] = m["ms"] / attn_ms
+    return res
+
+
+def layer_sides(B, w, host, ka, va, reps=10, warm=3):
+    """The steps either side of the attention step, timed alone (medians): rotary
+    embedding of the host's q and k, and the anchor's own causal attention."""
+    import torch
+    L, A, Hq, Hkv, d = w.local_len, w.anchor_len, w.n_q_heads, w.n_kv_heads, w.head_dim
+    qo, ko = torch.empty_like(host.q), torch.empty_like(host.k)
+    pos0 = w.host * L       # sequence position of the host block's first token
+    ms_q = _median_ms(lambda: B.apb_rope(host.q, pos0, 500000.0, out=qo), reps, warm)
+    ms_k = _median_ms(lambda: B.apb_rope(host.k, pos0, 500000.0, out=ko), reps, warm)
+    rope_bytes = 2.0 * (L * Hq * d + L * Hkv * d) * 2
+    res = {"rope_ms": ms_q + ms_k, "rope_gbs": rope_bytes / ((ms_q + ms_k) * 1e-3) / 1e9}
+    res["rope_frac_hbm_peak"] = res["rope_gbs"] / PEAK_HBM_GBS
+    if A:
+        pr = B.Problem(Hq, Hkv, d, L, A, w.pass_per_host, w.host, w.n_hosts, None)
+        qa = host.q[:A].contiguous()          # stand-in anchor queries of the anchor's shape
+        out = torch.empty((A, Hq, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((Hq, A), dtype=torch.float32, device="cuda")
+        ms = _median_ms(lambda: B.apb_anchor_attention(pr, qa, ka, va, out=out, lse=lse), reps, warm)
+        fl = 4.0 * d * Hq * (A * (A + 1) // 2)
+        res.update({"anchor_attention_ms": ms, "anchor_attention_tflops": fl / (ms * 1e-3) / 1e12})
     return res
 
 
@@ -318,6 +343,7 @@ def main():
         print("# split-phase attention and baseline modes", file=sys.stderr, flush=True)
         result["split_phase"] = split_phase(B, pr, host, ka, va, buf.k_pass, buf.v_pass, attn_ms)
         result["modes"] = baseline_modes(B, w, host, prior_kv, attn_ms)
+        result["layer_sides"] = layer_sides(B, w, host, ka, va)
     del buf, host, kcs, vcs, prior_kv
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle on a bounded sample)", file=sys.stderr, flush=True)

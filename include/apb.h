@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define APB_ABI_VERSION 2
+#define APB_ABI_VERSION 3
 
 /* Upper limits of this implementation (APB_ERR_UNSUPPORTED beyond them). */
 #define APB_MAX_Q_HEADS 256
@@ -206,6 +206,38 @@ apb_status apb_block_attention_segments(const apb_problem *problem, uint32_t seg
  */
 apb_status apb_merge_attention(const apb_problem *problem, const void *out_a, const float *lse_a,
                                const void *out_b, const float *lse_b, void *out, float *lse, void *stream);
+
+/*
+ * The steps on either side of step 4 in one layer on a host.
+ *
+ * Each host carries the anchor through the layer together with its local block
+ * (explainer, "APB 的主要功能": the anchor block, holding the start of the
+ * sequence, is prepended to every local block), so the anchor's own queries
+ * attend causally over the anchor: anchor row r sees anchor rows 0..r.
+ *   q_anchor            bf16 [A][Hq][d]
+ *   k_anchor, v_anchor  bf16 [A][Hkv][d]
+ *   out                 bf16 [A][Hq][d] (output)
+ *   lse                 fp32 [Hq][A]    (output, natural log) or NULL
+ * Requires A >= 1; uses the step-4 kernel.  Other arguments as apb_block_attention.
+ */
+apb_status apb_anchor_attention(const apb_problem *problem, const void *q_anchor, const void *k_anchor,
+                                const void *v_anchor, float softmax_scale, void *out, float *lse, void *stream);
+
+/*
+ * Rotary position embedding, rotate-half pairing, on a token-major tensor (the
+ * position encoding of the Llama models the pages evaluate on; q and k reach
+ * the steps above already rotated).  Row r sits at position pos0 + r; for head
+ * h and i < d/2, with theta_i = theta_base^(-2i/d) and a = (pos0 + r) * theta_i:
+ *     out[r][h][i]       = x[r][h][i] cos(a) - x[r][h][i + d/2] sin(a)
+ *     out[r][h][i + d/2] = x[r][h][i] sin(a) + x[r][h][i + d/2] cos(a)
+ *   x, out   bf16 [rows][heads][d], d in {64, 128}; out may be x (in place)
+ * theta_i is computed on the host in double precision, a is reduced modulo 2*pi
+ * in double precision on the device, the rotation is done in fp32 and rounded
+ * once to bf16 (nearest even).  rows >= 1, 1 <= heads <= 4096, pos0 >= 0,
+ * theta_base > 1 and finite.
+ */
+apb_status apb_rope(const void *x, void *out, int32_t rows, int32_t heads, int32_t head_dim, int64_t pos0,
+                    float theta_base, void *stream);
 
 /* Host-only checks of a problem description; launches nothing. */
 apb_status apb_validate_problem(const apb_problem *problem);

@@ -11,12 +11,14 @@ Plain, slow numpy in float64, one step per function, in the order the pages give
   3. concatenate the compressed blocks of the preceding hosts (the passing block),
   4. attention of the local queries over [anchor | passing | local, causal],
      also over any subset of those key segments, and the merge of two partial
-     results over disjoint key sets into the result over their union.
+     results over disjoint key sets into the result over their union;
+and, either side of step 4, rotary position embedding of q and k.
 
 Sources (web pages on APB, "Accelerating Distributed Long-Context Inference by
 Passing Compressed Context Blocks across GPUs"):
   * arXiv abstract (mlsanity.com/paper/2502.12085): multi-host approximate
-    attention that passes essential KV pairs; a tailored FlashAttn kernel.
+    attention that passes essential KV pairs, run by a FlashAttention kernel
+    adapted to APB.
   * juejin.cn explainer, section "APB 的主要功能": the input is split evenly over
     hosts and an anchor block holding the start of the sequence is prepended to
     each local block; each host compresses its KV cache with retaining heads;
@@ -232,6 +234,26 @@ def merge_attention(o_a, lse_a, o_b, lse_b):
     out = np.where(nonempty.T[:, :, None], c_a * o_a + c_b * o_b, 0.0)
     lse = np.where(nonempty, m_safe + np.log(den_safe), -np.inf)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Either side of step 4 (one layer on a host): the anchor's own causal
+# attention is block_attention with the anchor as the local block and no other
+# segment.  Rotary position embedding of q and k, rotate-half pairing (the
+# position encoding of the Llama models the pages evaluate on).
+# ---------------------------------------------------------------------------
+def rope(x, pos0: int, theta_base: float):
+    """float64 [rows, heads, d]: row r at position pos0 + r; pair (i, i + d/2)
+    rotated by the angle (pos0 + r) * theta_base^(-2i/d)."""
+    x = _f64(x)
+    rows, _, d = x.shape
+    half = d // 2
+    theta = float(theta_base) ** (-2.0 * np.arange(half) / d)
+    ang = (pos0 + np.arange(rows, dtype=np.float64))[:, None] * theta[None, :]   # [rows, d/2]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    x0, x1 = x[..., :half], x[..., half:]
+    return np.concatenate([x0 * c - x1 * s, x0 * s + x1 * c], axis=-1)
 
 
 def compress_host(q, k, v, weights, l: int, kv_head_of_q=None):

@@ -102,6 +102,10 @@ def lib() -> ctypes.CDLL:
                                                    c_void_p, c_void_p, c_void_p]
         L.apb_merge_attention.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                           c_void_p, c_void_p]
+        L.apb_anchor_attention.argtypes = [P, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p,
+                                           c_void_p]
+        L.apb_rope.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, ctypes.c_int64, c_float,
+                               c_void_p]
         L.apb_validate_problem.argtypes = [P]
         L.apb_status_string.argtypes = [c_int]
         L.apb_status_string.restype = c_char_p
@@ -109,8 +113,8 @@ def lib() -> ctypes.CDLL:
         L.apb_last_error.restype = c_char_p
         L.apb_abi_version.argtypes = []
         for name in ("apb_score_kv", "apb_topk_gather", "apb_build_passing", "apb_block_attention",
-                     "apb_block_attention_segments", "apb_merge_attention", "apb_validate_problem",
-                     "apb_abi_version"):
+                     "apb_block_attention_segments", "apb_merge_attention", "apb_anchor_attention",
+                     "apb_rope", "apb_validate_problem", "apb_abi_version"):
             getattr(L, name).restype = c_int
         _lib = L
     return _lib
@@ -315,6 +319,49 @@ def apb_merge_attention(problem: Problem, out_a, lse_a, out_b, lse_b, out=None, 
     del keep
     _check(st, "apb_merge_attention")
     return out, lse
+
+
+def apb_anchor_attention(problem: Problem, q_anchor, k_anchor, v_anchor,
+                         softmax_scale: Optional[float] = None, out=None, lse=True, stream=None):
+    """Causal attention of the anchor's queries over the anchor (see include/apb.h).
+
+    Returns (out bf16 [A, Hq, d], lse fp32 [Hq, A] or None).
+    """
+    pr = problem
+    A, Hq, Hkv, d = pr.anchor_len, pr.n_q_heads, pr.n_kv_heads, pr.head_dim
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    dev = q_anchor.device
+    if out is None:
+        out = torch.empty((A, Hq, d), dtype=torch.bfloat16, device=dev)
+    if lse is True:
+        lse = torch.empty((Hq, A), dtype=torch.float32, device=dev)
+    elif lse is False:
+        lse = None
+    cp, keep = pr.to_c()
+    st = lib().apb_anchor_attention(
+        ctypes.byref(cp), _ptr(q_anchor, "q_anchor", torch.bfloat16, (A, Hq, d)),
+        _ptr(k_anchor, "k_anchor", torch.bfloat16, (A, Hkv, d)),
+        _ptr(v_anchor, "v_anchor", torch.bfloat16, (A, Hkv, d)), float(softmax_scale),
+        _ptr(out, "out", torch.bfloat16, (A, Hq, d)), _ptr(lse, "lse", torch.float32, (Hq, A)),
+        _stream(stream))
+    del keep
+    _check(st, "apb_anchor_attention")
+    return out, lse
+
+
+def apb_rope(x, pos0: int, theta_base: float, out=None, stream=None):
+    """Rotary position embedding of bf16 x [rows, heads, d] (see include/apb.h); out may be x."""
+    if x.dim() != 3:
+        raise ValueError("x must be [rows, heads, head_dim]")
+    rows, heads, d = (int(n) for n in x.shape)
+    if out is None:
+        out = torch.empty_like(x)
+    st = lib().apb_rope(_ptr(x, "x", torch.bfloat16, (rows, heads, d)),
+                        _ptr(out, "out", torch.bfloat16, (rows, heads, d)), rows, heads, d, int(pos0),
+                        float(theta_base), _stream(stream))
+    _check(st, "apb_rope")
+    return out
 
 
 def apb_validate_problem(problem: Problem) -> int:

@@ -58,6 +58,16 @@ struct MergeArgs {
 };
 hipError_t launch_merge_attention(const MergeArgs &a, hipStream_t s);
 
+// Rotary position embedding (rotate-half pairing).
+struct RopeArgs {
+  const uint16_t *x;
+  uint16_t *out;
+  long long pos0;
+  int rows, heads, d;
+  double theta[64];         // theta_i = base^(-2i/d), i < d/2
+};
+hipError_t launch_rope(const RopeArgs &a, hipStream_t s);
+
 // Scorer: per kv head, 2-layer ReLU MLP over [q of the group; k; v].
 struct ScoreArgs {
   const uint16_t *q, *k, *v, *w1;

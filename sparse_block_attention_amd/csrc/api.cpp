@@ -171,6 +171,44 @@ apb_status block_attention(const apb_problem *pr, uint32_t segments, const void 
                     "apb_block_attention launch");
 }
 
+apb_status anchor_attention(const apb_problem *pr, const void *q, const void *k, const void *v, float scale,
+                            void *out, float *lse, void *stream) {
+  APB_TRY(apb_host::check_problem(pr));
+  if (pr->anchor_len < 1) return fail(APB_ERR_INVALID_ARGUMENT, "anchor attention needs anchor_len >= 1");
+  // The anchor's own rows as a local block: causal, no anchor, no passing.
+  apb_problem ap = *pr;
+  ap.local_len = pr->anchor_len;
+  ap.anchor_len = 0;
+  ap.pass_per_host = 0;
+  ap.host_index = 0;
+  ap.n_hosts = 1;
+  APB_TRY(apb_host::check_problem(&ap));
+  return block_attention(&ap, APB_SEG_LOCAL, q, nullptr, nullptr, nullptr, nullptr, k, v, scale, out, lse, stream);
+}
+
+apb_status rope(const void *x, void *out, int32_t rows, int32_t heads, int32_t d, int64_t pos0, float base,
+                void *stream) {
+  APB_TRY(need_ptr(x, "x"));
+  APB_TRY(need_ptr(out, "out"));
+  if (rows < 1) return fail(APB_ERR_INVALID_ARGUMENT, "rows = %d, need >= 1", rows);
+  if (heads < 1 || heads > 4096) return fail(APB_ERR_INVALID_ARGUMENT, "heads = %d, need 1..4096", heads);
+  if (d != 64 && d != 128) return fail(APB_ERR_UNSUPPORTED, "head_dim = %d, supported: 64, 128", d);
+  if (pos0 < 0 || pos0 + rows > (1LL << 53))
+    return fail(APB_ERR_INVALID_ARGUMENT, "pos0 = %lld: positions must lie in [0, 2^53)", (long long)pos0);
+  if (!(base > 1.f) || !isfinite(base))
+    return fail(APB_ERR_INVALID_ARGUMENT, "theta_base = %g, need finite and > 1", (double)base);
+  apb::RopeArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = static_cast<const uint16_t *>(x);
+  a.out = static_cast<uint16_t *>(out);
+  a.pos0 = pos0;
+  a.rows = rows;
+  a.heads = heads;
+  a.d = d;
+  for (int i = 0; i < d / 2; ++i) a.theta[i] = pow((double)base, -2.0 * i / d);
+  return hip_status(apb::launch_rope(a, static_cast<hipStream_t>(stream)), "apb_rope launch");
+}
+
 apb_status merge_attention(const apb_problem *pr, const void *oa, const float *la, const void *ob, const float *lb,
                            void *out, float *lse, void *stream) {
   APB_TRY(apb_host::check_problem(pr));
@@ -233,6 +271,16 @@ apb_status apb_block_attention_segments(const apb_problem *problem, uint32_t seg
                                         float softmax_scale, void *out, float *lse, void *stream) {
   APB_GUARD(block_attention(problem, segments, q_local, k_anchor, v_anchor, k_pass, v_pass, k_local, v_local,
                             softmax_scale, out, lse, stream));
+}
+
+apb_status apb_anchor_attention(const apb_problem *problem, const void *q_anchor, const void *k_anchor,
+                                const void *v_anchor, float softmax_scale, void *out, float *lse, void *stream) {
+  APB_GUARD(anchor_attention(problem, q_anchor, k_anchor, v_anchor, softmax_scale, out, lse, stream));
+}
+
+apb_status apb_rope(const void *x, void *out, int32_t rows, int32_t heads, int32_t head_dim, int64_t pos0,
+                    float theta_base, void *stream) {
+  APB_GUARD(rope(x, out, rows, heads, head_dim, pos0, theta_base, stream));
 }
 
 apb_status apb_merge_attention(const apb_problem *problem, const void *out_a, const float *lse_a, const void *out_b,

@@ -2,9 +2,9 @@
 //
 // Source: juejin.cn APB explainer, section "APB 的主要功能", bullet on
 // computation (each host attends over anchor, passing and local blocks), and the
-// arXiv abstract's "tailored FlashAttn kernel".  The mask reading (anchor and
-// passing fully visible, local keys causal) follows from every anchor and
-// passing token preceding every local token in the sequence.
+// arXiv abstract, which names a FlashAttention kernel adapted to APB.  The mask
+// reading (anchor and passing fully visible, local keys causal) follows from
+// every anchor and passing token preceding every local token in the sequence.
 //
 // gfx950 design (one code path, instantiated for head_dim 64 and 128):
 //  * Workgroup = NW wave64s; each wave owns 32*NSUB consecutive query rows of one

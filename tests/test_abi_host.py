@@ -56,7 +56,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert B.apb_abi_version() == 2
+    assert B.apb_abi_version() == 3
     assert B.apb_status_string(B.APB_OK) == "APB_OK"
     assert B.apb_status_string(B.APB_ERR_UNSUPPORTED) == "APB_ERR_UNSUPPORTED"
     assert B.apb_status_string(99) == "APB_ERR_UNKNOWN"
@@ -161,6 +161,30 @@ def test_merge_rejects_bad_arguments(lib):
     assert "lse" in B.apb_last_error()
     cp, keep = _problem(head_dim=96).to_c()
     assert lib.apb_merge_attention(ctypes.byref(cp), *good, None) == B.APB_ERR_UNSUPPORTED
+
+
+def test_anchor_attention_and_rope_reject_bad_arguments(lib):
+    cp, keep = _problem(anchor_len=0).to_c()
+    assert lib.apb_anchor_attention(ctypes.byref(cp), 0x1000, 0x2000, 0x3000, ctypes.c_float(0.1), 0x4000,
+                                    None, None) == B.APB_ERR_INVALID_ARGUMENT
+    assert "anchor_len" in B.apb_last_error()
+    cp, keep = _problem().to_c()
+    assert lib.apb_anchor_attention(ctypes.byref(cp), 0x1000, None, 0x3000, ctypes.c_float(0.1), 0x4000,
+                                    None, None) == B.APB_ERR_INVALID_ARGUMENT
+    assert "k_local" in B.apb_last_error()    # the anchor runs as a local block
+    good = dict(x=0x1000, out=0x2000, rows=4, heads=2, d=128, pos0=0, base=10000.0)
+    for bad, code, needle in [({"x": None}, B.APB_ERR_INVALID_ARGUMENT, "x"),
+                              ({"out": 0x2008}, B.APB_ERR_INVALID_ARGUMENT, "out"),
+                              ({"rows": 0}, B.APB_ERR_INVALID_ARGUMENT, "rows"),
+                              ({"heads": 5000}, B.APB_ERR_INVALID_ARGUMENT, "heads"),
+                              ({"d": 96}, B.APB_ERR_UNSUPPORTED, "head_dim"),
+                              ({"pos0": -1}, B.APB_ERR_INVALID_ARGUMENT, "pos0"),
+                              ({"base": 1.0}, B.APB_ERR_INVALID_ARGUMENT, "theta_base"),
+                              ({"base": float("inf")}, B.APB_ERR_INVALID_ARGUMENT, "theta_base")]:
+        a = dict(good, **bad)
+        st = lib.apb_rope(a["x"], a["out"], a["rows"], a["heads"], a["d"], a["pos0"], ctypes.c_float(a["base"]),
+                          None)
+        assert st == code and needle in B.apb_last_error(), (bad, st, B.apb_last_error())
 
 
 def test_score_rejects_bad_scorer(lib):

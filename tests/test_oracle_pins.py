@@ -259,6 +259,37 @@ def test_rows_with_no_visible_key():
     assert np.all(o == 0.0) and np.all(lse == -np.inf)
 
 
+# --------------------------------------------------------------------------- rotary embedding
+
+
+def test_rope_hand_values_and_position_zero():
+    """d = 2, theta_0 = 1: (1, 0) and (0, 1) at position 1 turn by one radian; position 0 is the identity."""
+    x = np.array([[[1.0, 0.0]], [[0.0, 1.0]]])                      # rows at positions 1 and 2
+    o = orc.rope(x, 1, 10000.0)
+    np.testing.assert_allclose(o[0, 0], [np.cos(1.0), np.sin(1.0)], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(o[1, 0], [-np.sin(2.0), np.cos(2.0)], rtol=0, atol=1e-15)
+    y = _rand((3, 2, 8), 90)
+    assert np.array_equal(orc.rope(y[:1], 0, 500000.0), y[:1])
+
+
+def test_rope_is_a_rotation_by_relative_position():
+    """Pair norms are kept; <R(p) q, R(p') k> depends on p - p' only; R(a) then R(b) is R(a + b)."""
+    q, k = _rand((1, 1, 64), 91), _rand((1, 1, 64), 92)
+    base = 10000.0
+    rq = orc.rope(np.repeat(q, 40, axis=0), 0, base)                # q at positions 0..39
+    rk = orc.rope(np.repeat(k, 40, axis=0), 0, base)
+    for p, pk in [(5, 2), (17, 14), (39, 36)]:                      # all three differ by 3
+        np.testing.assert_allclose(rq[p, 0] @ rk[pk, 0], rq[5, 0] @ rk[2, 0], rtol=1e-12)
+    x = _rand((4, 3, 128), 93)
+    o = orc.rope(x, 1000, 500000.0)
+    norm = lambda t: t[..., :64] ** 2 + t[..., 64:] ** 2
+    np.testing.assert_allclose(norm(o), norm(x), rtol=1e-12)
+    # composition: a row at position 7 turned again by 5 equals the row at position 12
+    x1 = x[:1]
+    np.testing.assert_allclose(orc.rope(orc.rope(x1, 7, 500000.0), 5, 500000.0), orc.rope(x1, 12, 500000.0),
+                               rtol=1e-9, atol=1e-12)
+
+
 # --------------------------------------------------------------------------- scorer
 
 
