@@ -22,8 +22,9 @@ outside the step:
     with, at the same layer shape: Star Attention (anchor = the whole first
     block, no passing block) and full causal FlashAttention-style attention of
     the last host (every earlier token visible, no anchor);
-  * `layer_sides`: rotary embedding of the host's q and k, and the anchor's
-    own causal attention (steps either side of the attention step).
+  * `layer_sides`: the QKV projection of the host block, rotary embedding of
+    its q and k, and the anchor's own causal attention (steps either side of
+    the attention step).
 """
 from __future__ import annotations
 
@@ -171,6 +172,21 @@ def layer_sides(B, w, host, ka, va, reps=10, warm=3):
     rope_bytes = 2.0 * (L * Hq * d + L * Hkv * d) * 2
     res = {"rope_ms": ms_q + ms_k, "rope_gbs": rope_bytes / ((ms_q + ms_k) * 1e-3) / 1e9}
     res["rope_frac_hbm_peak"] = res["rope_gbs"] / PEAK_HBM_GBS
+    # QKV projection of the host block from hidden states of width Hq*d (the
+    # Llama layout: hidden = Hq * d), synthetic weights
+    from sparse_block_attention_amd import synth
+    from sparse_block_attention_amd.tensors import to_device_bf16
+    hidden = Hq * d
+    xs = torch.randn((L, hidden), dtype=torch.float32, device="cuda").to(torch.bfloat16)
+    wts = [to_device_bf16(synth.random_bf16((n * d, hidden), 40 + i, sigma=hidden ** -0.5))
+           for i, n in enumerate((Hq, Hkv, Hkv))]
+    prp = B.Problem(Hq, Hkv, d, L, A, w.pass_per_host, w.host, w.n_hosts, None)
+    qo2, ko2, vo2 = torch.empty_like(host.q), torch.empty_like(host.k), torch.empty_like(host.v)
+    ms = _median_ms(lambda: B.apb_qkv_projection(prp, xs, *wts, q=qo2, k=ko2, v=vo2), reps, warm)
+    fl = 2.0 * L * hidden * (Hq + 2 * Hkv) * d
+    res.update({"qkv_projection_ms": ms, "qkv_projection_tflops": fl / (ms * 1e-3) / 1e12,
+                "qkv_projection_frac_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
+    del xs, wts, qo2, ko2, vo2
     if A:
         pr = B.Problem(Hq, Hkv, d, L, A, w.pass_per_host, w.host, w.n_hosts, None)
         qa = host.q[:A].contiguous()          # stand-in anchor queries of the anchor's shape

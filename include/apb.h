@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define APB_ABI_VERSION 3
+#define APB_ABI_VERSION 4
 
 /* Upper limits of this implementation (APB_ERR_UNSUPPORTED beyond them). */
 #define APB_MAX_Q_HEADS 256
@@ -238,6 +238,22 @@ apb_status apb_anchor_attention(const apb_problem *problem, const void *q_anchor
  */
 apb_status apb_rope(const void *x, void *out, int32_t rows, int32_t heads, int32_t head_dim, int64_t pos0,
                     float theta_base, void *stream);
+
+/*
+ * QKV projection of `rows` hidden-state rows of a host (its local block, or
+ * the anchor it carries), before step 1: with nn.Linear weights [out][in],
+ *     q = x Wq^T,  k = x Wk^T,  v = x Wv^T
+ *   x        bf16 [rows][hidden]
+ *   wq       bf16 [Hq*d][hidden];   wk, wv  bf16 [Hkv*d][hidden]
+ *   q        bf16 [rows][Hq][d];    k, v    bf16 [rows][Hkv][d]   (outputs)
+ * Products of bf16 values accumulate in fp32; each output is rounded once to
+ * bf16 (nearest even).  hidden: a multiple of 32, 32..1048576; 1 <= rows <=
+ * APB_MAX_LOCAL_LEN.  Only n_q_heads, n_kv_heads and head_dim of `problem` are
+ * used, but the whole problem must be valid.
+ */
+apb_status apb_qkv_projection(const apb_problem *problem, int32_t rows, int32_t hidden, const void *x,
+                              const void *wq, const void *wk, const void *wv, void *q, void *k, void *v,
+                              void *stream);
 
 /* Host-only checks of a problem description; launches nothing. */
 apb_status apb_validate_problem(const apb_problem *problem);

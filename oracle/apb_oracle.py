@@ -12,7 +12,8 @@ Plain, slow numpy in float64, one step per function, in the order the pages give
   4. attention of the local queries over [anchor | passing | local, causal],
      also over any subset of those key segments, and the merge of two partial
      results over disjoint key sets into the result over their union;
-and, either side of step 4, rotary position embedding of q and k.
+and, either side of step 4, the QKV projection and rotary position embedding of
+q and k.
 
 Sources (web pages on APB, "Accelerating Distributed Long-Context Inference by
 Passing Compressed Context Blocks across GPUs"):
@@ -242,6 +243,16 @@ def merge_attention(o_a, lse_a, o_b, lse_b):
 # segment.  Rotary position embedding of q and k, rotate-half pairing (the
 # position encoding of the Llama models the pages evaluate on).
 # ---------------------------------------------------------------------------
+def qkv_projection(x, wq, wk, wv, n_q_heads: int, n_kv_heads: int):
+    """float64 (q [rows, Hq, d], k, v [rows, Hkv, d]) = x W^T for nn.Linear weights [out][in]."""
+    x = _f64(x)
+    rows = x.shape[0]
+    q = (x @ _f64(wq).T).reshape(rows, n_q_heads, -1)
+    k = (x @ _f64(wk).T).reshape(rows, n_kv_heads, -1)
+    v = (x @ _f64(wv).T).reshape(rows, n_kv_heads, -1)
+    return q, k, v
+
+
 def rope(x, pos0: int, theta_base: float):
     """float64 [rows, heads, d]: row r at position pos0 + r; pair (i, i + d/2)
     rotated by the angle (pos0 + r) * theta_base^(-2i/d)."""

@@ -106,6 +106,8 @@ def lib() -> ctypes.CDLL:
                                            c_void_p]
         L.apb_rope.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, ctypes.c_int64, c_float,
                                c_void_p]
+        L.apb_qkv_projection.argtypes = [P, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p]
         L.apb_validate_problem.argtypes = [P]
         L.apb_status_string.argtypes = [c_int]
         L.apb_status_string.restype = c_char_p
@@ -114,7 +116,7 @@ def lib() -> ctypes.CDLL:
         L.apb_abi_version.argtypes = []
         for name in ("apb_score_kv", "apb_topk_gather", "apb_build_passing", "apb_block_attention",
                      "apb_block_attention_segments", "apb_merge_attention", "apb_anchor_attention",
-                     "apb_rope", "apb_validate_problem", "apb_abi_version"):
+                     "apb_rope", "apb_qkv_projection", "apb_validate_problem", "apb_abi_version"):
             getattr(L, name).restype = c_int
         _lib = L
     return _lib
@@ -362,6 +364,30 @@ def apb_rope(x, pos0: int, theta_base: float, out=None, stream=None):
                         float(theta_base), _stream(stream))
     _check(st, "apb_rope")
     return out
+
+
+def apb_qkv_projection(problem: Problem, x, wq, wk, wv, q=None, k=None, v=None, stream=None):
+    """q, k, v of hidden states x [rows, hidden] (see include/apb.h): (q, k, v) bf16."""
+    pr = problem
+    Hq, Hkv, d = pr.n_q_heads, pr.n_kv_heads, pr.head_dim
+    rows, hidden = (int(n) for n in x.shape)
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, Hq, d), dtype=torch.bfloat16, device=dev)
+    if k is None:
+        k = torch.empty((rows, Hkv, d), dtype=torch.bfloat16, device=dev)
+    if v is None:
+        v = torch.empty((rows, Hkv, d), dtype=torch.bfloat16, device=dev)
+    cp, keep = pr.to_c()
+    st = lib().apb_qkv_projection(
+        ctypes.byref(cp), rows, hidden, _ptr(x, "x", torch.bfloat16, (rows, hidden)),
+        _ptr(wq, "wq", torch.bfloat16, (Hq * d, hidden)), _ptr(wk, "wk", torch.bfloat16, (Hkv * d, hidden)),
+        _ptr(wv, "wv", torch.bfloat16, (Hkv * d, hidden)), _ptr(q, "q", torch.bfloat16, (rows, Hq, d)),
+        _ptr(k, "k", torch.bfloat16, (rows, Hkv, d)), _ptr(v, "v", torch.bfloat16, (rows, Hkv, d)),
+        _stream(stream))
+    del keep
+    _check(st, "apb_qkv_projection")
+    return q, k, v
 
 
 def apb_validate_problem(problem: Problem) -> int:

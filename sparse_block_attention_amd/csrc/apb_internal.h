@@ -58,6 +58,15 @@ struct MergeArgs {
 };
 hipError_t launch_merge_attention(const MergeArgs &a, hipStream_t s);
 
+// C[M][N] = X[M][K] W[N][K]^T in bf16, fp32 accumulation (QKV projection).
+struct ProjArgs {
+  const uint16_t *x, *w;
+  uint16_t *c;
+  int M, N, K;              // N % 4 == 0, K % 32 == 0
+  int n_mt, n_nt;           // tiles of 256 along M and N
+};
+hipError_t launch_proj_gemm(ProjArgs &a, hipStream_t s);
+
 // Rotary position embedding (rotate-half pairing).
 struct RopeArgs {
   const uint16_t *x;

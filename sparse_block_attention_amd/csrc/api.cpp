@@ -209,6 +209,37 @@ apb_status rope(const void *x, void *out, int32_t rows, int32_t heads, int32_t d
   return hip_status(apb::launch_rope(a, static_cast<hipStream_t>(stream)), "apb_rope launch");
 }
 
+apb_status qkv_projection(const apb_problem *pr, int32_t rows, int32_t hidden, const void *x, const void *wq,
+                          const void *wk, const void *wv, void *q, void *k, void *v, void *stream) {
+  APB_TRY(apb_host::check_problem(pr));
+  if (rows < 1 || rows > APB_MAX_LOCAL_LEN)
+    return fail(APB_ERR_INVALID_ARGUMENT, "rows = %d, need 1..%d", rows, APB_MAX_LOCAL_LEN);
+  if (hidden < 32 || hidden > (1 << 20) || hidden % 32 != 0)
+    return fail(APB_ERR_UNSUPPORTED, "hidden = %d, supported: multiples of 32 in [32, 2^20]", hidden);
+  const void *ins[4] = {x, wq, wk, wv};
+  const char *in_names[4] = {"x", "wq", "wk", "wv"};
+  for (int i = 0; i < 4; ++i) APB_TRY(need_ptr(ins[i], in_names[i]));
+  APB_TRY(need_ptr(q, "q"));
+  APB_TRY(need_ptr(k, "k"));
+  APB_TRY(need_ptr(v, "v"));
+  const int d = pr->head_dim;
+  const int outs[3] = {pr->n_q_heads * d, pr->n_kv_heads * d, pr->n_kv_heads * d};
+  const void *ws[3] = {wq, wk, wv};
+  void *cs[3] = {q, k, v};
+  for (int i = 0; i < 3; ++i) {
+    apb::ProjArgs a;
+    memset(&a, 0, sizeof a);
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = static_cast<const uint16_t *>(ws[i]);
+    a.c = static_cast<uint16_t *>(cs[i]);
+    a.M = rows;
+    a.N = outs[i];
+    a.K = hidden;
+    APB_TRY(hip_status(apb::launch_proj_gemm(a, static_cast<hipStream_t>(stream)), "apb_qkv_projection launch"));
+  }
+  return APB_OK;
+}
+
 apb_status merge_attention(const apb_problem *pr, const void *oa, const float *la, const void *ob, const float *lb,
                            void *out, float *lse, void *stream) {
   APB_TRY(apb_host::check_problem(pr));
@@ -281,6 +312,12 @@ apb_status apb_anchor_attention(const apb_problem *problem, const void *q_anchor
 apb_status apb_rope(const void *x, void *out, int32_t rows, int32_t heads, int32_t head_dim, int64_t pos0,
                     float theta_base, void *stream) {
   APB_GUARD(rope(x, out, rows, heads, head_dim, pos0, theta_base, stream));
+}
+
+apb_status apb_qkv_projection(const apb_problem *problem, int32_t rows, int32_t hidden, const void *x,
+                              const void *wq, const void *wk, const void *wv, void *q, void *k, void *v,
+                              void *stream) {
+  APB_GUARD(qkv_projection(problem, rows, hidden, x, wq, wk, wv, q, k, v, stream));
 }
 
 apb_status apb_merge_attention(const apb_problem *problem, const void *out_a, const float *lse_a, const void *out_b,

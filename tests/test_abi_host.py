@@ -56,7 +56,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert B.apb_abi_version() == 3
+    assert B.apb_abi_version() == 4
     assert B.apb_status_string(B.APB_OK) == "APB_OK"
     assert B.apb_status_string(B.APB_ERR_UNSUPPORTED) == "APB_ERR_UNSUPPORTED"
     assert B.apb_status_string(99) == "APB_ERR_UNKNOWN"
@@ -185,6 +185,20 @@ def test_anchor_attention_and_rope_reject_bad_arguments(lib):
         st = lib.apb_rope(a["x"], a["out"], a["rows"], a["heads"], a["d"], a["pos0"], ctypes.c_float(a["base"]),
                           None)
         assert st == code and needle in B.apb_last_error(), (bad, st, B.apb_last_error())
+
+
+def test_qkv_projection_rejects_bad_arguments(lib):
+    cp, keep = _problem().to_c()
+    good = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000]
+    assert lib.apb_qkv_projection(ctypes.byref(cp), 0, 64, *good, None) == B.APB_ERR_INVALID_ARGUMENT
+    assert "rows" in B.apb_last_error()
+    assert lib.apb_qkv_projection(ctypes.byref(cp), 4, 48, *good, None) == B.APB_ERR_UNSUPPORTED
+    assert "hidden" in B.apb_last_error()
+    for i, name in enumerate(["x", "wq", "wk", "wv", "q", "k", "v"]):
+        args = list(good)
+        args[i] = None if i % 2 else good[i] + 8
+        assert lib.apb_qkv_projection(ctypes.byref(cp), 4, 64, *args, None) == B.APB_ERR_INVALID_ARGUMENT
+        assert name in B.apb_last_error()
 
 
 def test_score_rejects_bad_scorer(lib):

@@ -1,5 +1,6 @@
 """The steps either side of the attention step in one layer on a host: the
-anchor's own causal attention and rotary position embedding, HIP path vs oracle."""
+anchor's own causal attention, rotary position embedding and the QKV
+projection, HIP path vs oracle."""
 import numpy as np
 import pytest
 import torch
@@ -51,3 +52,25 @@ def test_rope_matches_oracle(rows, heads, d, pos0, base):
     B.apb_rope(xd, pos0, base, out=xd)
     torch.cuda.synchronize()
     assert torch.equal(xd, o)
+
+
+@pytest.mark.parametrize("rows,hidden,Hq,Hkv,d", [(1, 32, 2, 1, 64), (300, 96, 4, 2, 64),
+                                                  (700, 512, 6, 3, 128), (16384, 4096, 32, 8, 128)])
+def test_qkv_projection_matches_oracle(rows, hidden, Hq, Hkv, d):
+    """Ragged token and output tiles, K from one chunk to 4096.  Bar: one bf16 rounding of an
+    fp32 sum (half an ulp, 2^-9 relative) plus fp32 summation error, bounded by
+    4 sqrt(K) 2^-24 sum|x_i w_i|:  |o - o_ref| <= 2^-8 |o_ref| + 4 sqrt(K) 2^-24 sum|x_i w_i|."""
+    x = synth.random_bf16((rows, hidden), 5, stream=rows)
+    ws = [synth.random_bf16((n * d, hidden), 6 + i, sigma=hidden ** -0.5, stream=rows)
+          for i, n in enumerate((Hq, Hkv, Hkv))]
+    pr = B.Problem(Hq, Hkv, d, 64, 0, 0, 0, 1, None)
+    q, k, v = B.apb_qkv_projection(pr, to_device_bf16(x), *[to_device_bf16(w) for w in ws])
+    torch.cuda.synchronize()
+    sample = np.arange(rows) if rows <= 1024 else np.unique(np.r_[0, 255, 256, rows - 1,
+                                                                  np.random.default_rng(0).integers(0, rows, 60)])
+    refs = orc.qkv_projection(x[sample], *ws, Hq, Hkv)
+    bounds = orc.qkv_projection(np.abs(x[sample]), *[np.abs(w) for w in ws], Hq, Hkv)
+    for name, got, ref, bnd in zip("qkv", (q, k, v), refs, bounds):
+        g = from_device_bf16(got)[sample].astype(np.float64)
+        tol = 2.0 ** -8 * np.abs(ref) + 4 * np.sqrt(hidden) * 2.0 ** -24 * bnd
+        assert np.all(np.abs(g - ref) <= tol), (name, float(np.max(np.abs(g - ref) - tol)))

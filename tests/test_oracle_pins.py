@@ -259,6 +259,31 @@ def test_rows_with_no_visible_key():
     assert np.all(o == 0.0) and np.all(lse == -np.inf)
 
 
+# --------------------------------------------------------------------------- QKV projection
+
+
+def test_qkv_projection_reads_the_weight_rows():
+    """One-hot weight rows copy single input features into chosen output slots; zero rows give
+    zero; the output is linear in x (brute-force dot products on a tiny case)."""
+    rows, hidden, Hq, Hkv, d = 3, 8, 2, 1, 4
+    x = _rand((rows, hidden), 95)
+    wq = np.zeros((Hq * d, hidden))
+    wq[5, 2] = 1.0                                   # q head 1, dim 1 <- feature 2
+    wk = np.zeros((Hkv * d, hidden))
+    wk[3, 7] = -2.0                                  # k dim 3 <- -2 * feature 7
+    wv = _rand((Hkv * d, hidden), 96)
+    q, k, v = orc.qkv_projection(x, wq, wk, wv, Hq, Hkv)
+    assert q.shape == (rows, Hq, d) and k.shape == (rows, Hkv, d)
+    np.testing.assert_array_equal(q[:, 1, 1], x[:, 2])
+    assert np.count_nonzero(q) == np.count_nonzero(x[:, 2])
+    np.testing.assert_array_equal(k[:, 0, 3], -2.0 * x[:, 7])
+    for r in range(rows):
+        for c in range(d):
+            assert abs(v[r, 0, c] - sum(x[r, i] * wv[c, i] for i in range(hidden))) < 1e-12
+    q2, _, _ = orc.qkv_projection(3.0 * x, wq, wk, wv, Hq, Hkv)
+    np.testing.assert_allclose(q2, 3.0 * q, rtol=1e-15)
+
+
 # --------------------------------------------------------------------------- rotary embedding
 
 
