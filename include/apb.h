@@ -249,7 +249,8 @@ apb_status apb_rope(const void *x, void *out, int32_t rows, int32_t heads, int32
  * Products of bf16 values accumulate in fp32; each output is rounded once to
  * bf16 (nearest even).  hidden: a multiple of 32, 32..1048576; 1 <= rows <=
  * APB_MAX_LOCAL_LEN.  Only n_q_heads, n_kv_heads and head_dim of `problem` are
- * used, but the whole problem must be valid.
+ * used, but the whole problem must be valid.  One kernel launch computes q, k
+ * and v.
  */
 apb_status apb_qkv_projection(const apb_problem *problem, int32_t rows, int32_t hidden, const void *x,
                               const void *wq, const void *wk, const void *wv, void *q, void *k, void *v,

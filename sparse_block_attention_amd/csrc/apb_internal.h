@@ -59,11 +59,16 @@ struct MergeArgs {
 hipError_t launch_merge_attention(const MergeArgs &a, hipStream_t s);
 
 // C[M][N] = X[M][K] W[N][K]^T in bf16, fp32 accumulation (QKV projection).
+// One launch covers the three weight matrices (q, k, v); their 256-wide output
+// slices are numbered one after another.
 struct ProjArgs {
-  const uint16_t *x, *w;
-  uint16_t *c;
-  int M, N, K;              // N % 4 == 0, K % 32 == 0
-  int n_mt, n_nt;           // tiles of 256 along M and N
+  const uint16_t *x;
+  const uint16_t *w[3];
+  uint16_t *c[3];
+  int N[3];                 // outputs of each matrix, N % 4 == 0
+  int M, K;                 // K % 32 == 0
+  int n_mt, n_nt;           // tiles of 256 along M; slices of 256 over all three N
+  int slice_end[3];         // cumulative slice counts
 };
 hipError_t launch_proj_gemm(ProjArgs &a, hipStream_t s);
 

@@ -223,20 +223,21 @@ apb_status qkv_projection(const apb_problem *pr, int32_t rows, int32_t hidden, c
   APB_TRY(need_ptr(k, "k"));
   APB_TRY(need_ptr(v, "v"));
   const int d = pr->head_dim;
-  const int outs[3] = {pr->n_q_heads * d, pr->n_kv_heads * d, pr->n_kv_heads * d};
-  const void *ws[3] = {wq, wk, wv};
-  void *cs[3] = {q, k, v};
-  for (int i = 0; i < 3; ++i) {
-    apb::ProjArgs a;
-    memset(&a, 0, sizeof a);
-    a.x = static_cast<const uint16_t *>(x);
-    a.w = static_cast<const uint16_t *>(ws[i]);
-    a.c = static_cast<uint16_t *>(cs[i]);
-    a.M = rows;
-    a.N = outs[i];
-    a.K = hidden;
-    APB_TRY(hip_status(apb::launch_proj_gemm(a, static_cast<hipStream_t>(stream)), "apb_qkv_projection launch"));
-  }
+  apb::ProjArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = static_cast<const uint16_t *>(x);
+  a.w[0] = static_cast<const uint16_t *>(wq);
+  a.w[1] = static_cast<const uint16_t *>(wk);
+  a.w[2] = static_cast<const uint16_t *>(wv);
+  a.c[0] = static_cast<uint16_t *>(q);
+  a.c[1] = static_cast<uint16_t *>(k);
+  a.c[2] = static_cast<uint16_t *>(v);
+  a.N[0] = pr->n_q_heads * d;
+  a.N[1] = pr->n_kv_heads * d;
+  a.N[2] = pr->n_kv_heads * d;
+  a.M = rows;
+  a.K = hidden;
+  APB_TRY(hip_status(apb::launch_proj_gemm(a, static_cast<hipStream_t>(stream)), "apb_qkv_projection launch"));
   return APB_OK;
 }
 

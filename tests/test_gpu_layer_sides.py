@@ -55,7 +55,8 @@ def test_rope_matches_oracle(rows, heads, d, pos0, base):
 
 
 @pytest.mark.parametrize("rows,hidden,Hq,Hkv,d", [(1, 32, 2, 1, 64), (300, 96, 4, 2, 64),
-                                                  (700, 512, 6, 3, 128), (16384, 4096, 32, 8, 128)])
+                                                  (513, 160, 3, 1, 64), (700, 512, 6, 3, 128),
+                                                  (16384, 4096, 32, 8, 128)])
 def test_qkv_projection_matches_oracle(rows, hidden, Hq, Hkv, d):
     """Ragged token and output tiles, K from one chunk to 4096.  Bar: one bf16 rounding of an
     fp32 sum (half an ulp, 2^-9 relative) plus fp32 summation error, bounded by
