@@ -34,6 +34,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // so a buffer everyone has finished reading may be overwritten after it.
 __device__ __forceinline__ void barrier_keep_dma() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// The same barrier built from compiler builtins (s_waitcnt lgkmcnt(0), then
+// s_barrier): the compiler then knows this wave's LDS reads have landed and adds
+// no wait of its own before later uses of their results.
+__device__ __forceinline__ void barrier_lds_drained() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maximum (no wait)
+  __builtin_amdgcn_s_barrier();
+}
+
 // Attention over [anchor | passing | local causal].
 struct AttnArgs {
   const uint16_t *q, *ka, *va, *kp, *vp, *kl, *vl;

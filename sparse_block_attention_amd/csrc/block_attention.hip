@@ -215,15 +215,20 @@ void block_attention_kernel(const AttnArgs a) {
   const int nL = a.use_local ? (last_row + BN - 1) / BN : 0;
   const int n_tiles = nA + nP + nL;
 
+  // Segment pointers and lengths are read from the arguments once, here; the
+  // per-tile choice is then a scalar select rather than a fresh argument load
+  // (and its wait) at the top of every tile.
+  const uint16_t *const seg_k[3] = {a.ka, a.kp, a.kl};
+  const uint16_t *const seg_v[3] = {a.va, a.vp, a.vl};
+  const int seg_n[3] = {a.A, a.P, a.L};
   auto tile_ref = [&](int t) {
     TileRef r;
-    if (t < nA) {
-      r.k = a.ka; r.v = a.va; r.k0 = t * BN; r.seg_len = a.A; r.seg = 0;
-    } else if (t < nA + nP) {
-      r.k = a.kp; r.v = a.vp; r.k0 = (t - nA) * BN; r.seg_len = a.P; r.seg = 1;
-    } else {
-      r.k = a.kl; r.v = a.vl; r.k0 = (t - nA - nP) * BN; r.seg_len = a.L; r.seg = 2;
-    }
+    const int sg = t < nA ? 0 : (t < nA + nP ? 1 : 2);
+    r.seg = sg;
+    r.k = sg == 0 ? seg_k[0] : (sg == 1 ? seg_k[1] : seg_k[2]);
+    r.v = sg == 0 ? seg_v[0] : (sg == 1 ? seg_v[1] : seg_v[2]);
+    r.seg_len = sg == 0 ? seg_n[0] : (sg == 1 ? seg_n[1] : seg_n[2]);
+    r.k0 = (t - (sg == 0 ? 0 : (sg == 1 ? nA : nA + nP))) * BN;
     return r;
   };
 
@@ -251,7 +256,13 @@ void block_attention_kernel(const AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[s][db] = f32x16{};
   }
-  const float sl2 = a.scale_log2;
+  // The softmax scale is first used inside the tile loop.  The empty asm reads
+  // it here, so its scalar load has landed before the loop.  Otherwise the load
+  // would be outstanding at the loop's first waits, and since scalar loads can
+  // return out of order, every wait for an LDS read in the loop would have to be
+  // a full lgkmcnt(0) instead of waiting for just the reads it needs.
+  float sl2 = a.scale_log2;
+  asm volatile("" : "+s"(sl2));
 
   // ---- prologue
   __syncthreads();  // LDS zeroed before the first DMA lands

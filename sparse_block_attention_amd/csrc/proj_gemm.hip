@@ -63,14 +63,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
-// Barrier after this wave's LDS reads have completed (s_waitcnt lgkmcnt(0)),
-// with LDS-DMA loads left in flight.  Both halves are builtins, so the compiler
-// knows the reads have landed and adds no wait of its own before their uses.
-__device__ __forceinline__ void barrier_lds_drained() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maximum (no wait)
-  __builtin_amdgcn_s_barrier();
-}
-
 // Operand fragments of one 16-wide K step: four token blocks, four output blocks.
 struct ProjFrags {
   bf16x8 x[4];
