@@ -14,8 +14,13 @@ Prints one JSON line.  `value` is prefill tokens/s of the host block (L / step
 time); `roofline` covers the attention kernel (HIP events around its launches);
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
 
-Two extra objects (skipped with --no-extras) time the same attention kernel
-outside the step:
+Extra objects (skipped with --no-extras):
+  * `stages`: each step of the path alone on one stream (median and min of 20
+    HIP-event timings, each behind a short spin kernel so that host overhead
+    stays outside the events), warm and with the Infinity Cache evicted before
+    every rep, with its algorithmic bytes (or FLOPs) and fraction of the HBM (or bf16
+    MFMA) peak, and scoring + top-l + gather combined; `sclk_mhz_after` is the
+    shader clock rocm-smi reports right after;
   * `split_phase`: anchor + local, then passing, then the merge of the two
     partial results (what lets the exchange between hosts overlap compute);
   * `modes`: the per-host attention of the two baselines the pages compare APB
@@ -104,6 +109,113 @@ def _median_ms(fn, reps: int, warm: int) -> float:
         b.record()
     torch.cuda.synchronize()
     return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def _stage_times(fn, reps: int, warm: int, evict=None):
+    """Median and min (ms) of `reps` HIP-event timings of fn().  Before every rep a
+    spin kernel that touches no memory holds the GPU for ~0.2 ms, so the host has
+    queued fn()'s kernels before the start event is reached: the events then bracket
+    GPU time only, not the host-side argument marshalling of a short kernel.  With
+    `evict`, it runs before the spin (cold caches)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        if evict is not None:
+            evict()
+        torch.cuda._sleep(400_000)
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in ev]
+    return float(np.median(t)), float(np.min(t))
+
+
+def stages(B, w, pr, sc, host, ka, va, kcs, vcs, buf, reps=20, warm=5):
+    """Each step of the path alone on one stream: score (a1), top-l + gather (a2+a3),
+    passing build (a5) and attention (a6).  Warm: inputs as the previous rep left the
+    caches.  Cold: a 512 MB buffer is written before every rep, outside the timed region,
+    which evicts the 256 MB Infinity Cache."""
+    import torch
+    L, Hq, Hkv, d, l, hs = (w.local_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.pass_per_host,
+                            w.hidden)
+    g = Hq // Hkv
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    fill = [0]
+
+    def evict():
+        fill[0] = (fill[0] + 1) & 0xFF
+        scratch.fill_(fill[0])
+
+    byt = {
+        # q, k, v of the block, W1, b1, w2 and b2 read; fp32 scores written
+        "a1_score": L * (Hq + 2 * Hkv) * d * 2 + Hkv * hs * (g + 2) * d * 2 + Hkv * (2 * hs + 1) * 4
+        + Hkv * L * 4,
+        # scores read; l rows of K and V per kv head read and written; indices written
+        "a2a3_topl_gather": Hkv * L * 4 + 2 * 2 * l * Hkv * d * 2 + Hkv * l * 4,
+        # p compressed blocks of K and V read and written once
+        "a5_passing": 2 * 2 * pr.pass_len * Hkv * d * 2,
+    }
+    fns = {
+        "a1_score": lambda: B.apb_score_kv(pr, sc, host.q, host.k, host.v, scores=buf.scores),
+        "a2a3_topl_gather": lambda: B.apb_topk_gather(pr, buf.scores, host.k, host.v, idx=buf.idx,
+                                                      k_comp=buf.k_comp, v_comp=buf.v_comp),
+    }
+    if pr.pass_len:
+        fns["a5_passing"] = lambda: B.apb_build_passing(pr, kcs, vcs, k_pass=buf.k_pass, v_pass=buf.v_pass)
+    fns["a6_attention"] = lambda: B.apb_block_attention(pr, host.q, ka, va, buf.k_pass, buf.v_pass, host.k,
+                                                        host.v, out=buf.out, lse=buf.lse)
+    res = {}
+    for name, fn in fns.items():
+        med, mn = _stage_times(fn, reps, warm)
+        r = {"us_median": med * 1e3, "us_min": mn * 1e3}
+        if name in byt:
+            cmed, cmn = _stage_times(fn, reps, warm, evict=evict)
+            r.update({"cold_us_median": cmed * 1e3, "cold_us_min": cmn * 1e3, "bytes": byt[name],
+                      "gbs": byt[name] / (med * 1e-3) / 1e9, "cold_gbs": byt[name] / (cmed * 1e-3) / 1e9})
+            r["frac_hbm_peak"] = r["gbs"] / PEAK_HBM_GBS
+            r["cold_frac_hbm_peak"] = r["cold_gbs"] / PEAK_HBM_GBS
+        else:
+            fl = attention_flops(w)
+            r.update({"tflops": fl / (med * 1e-3) / 1e12, "frac_bf16_peak": fl / (med * 1e-3) / 1e12
+                      / PEAK_BF16_TFLOPS})
+        res[name] = r
+    # scoring + top-l + gather together: their bytes over their summed time
+    for tag in ("", "cold_"):
+        t = res["a1_score"][tag + "us_median"] + res["a2a3_topl_gather"][tag + "us_median"]
+        b = byt["a1_score"] + byt["a2a3_topl_gather"]
+        res[tag + "a1_a3"] = {"us_median": t, "gbs": b / (t * 1e-6) / 1e9,
+                              "frac_hbm_peak": b / (t * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    del scratch
+    return res
+
+
+def sclk_mhz():
+    """Current shader clock of GPU 0 as rocm-smi reports it (MHz), or None."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                             timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r"sclk[^\n]*?\((\d+)\s*Mhz\)", out, re.IGNORECASE)
+    return int(m.group(1)) if m else None
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def split_phase(B, pr, host, ka, va, kp, vp, attn_ms, reps=10, warm=3):
@@ -237,6 +349,7 @@ def cpu_baseline(w, blocks, weights, anchor, n_rows=4096):
                    f"{w.n_q_heads} heads ({sample_pairs} of {all_pairs} visible pairs per head, "
                    f"scaled by the pair count); float64 numpy"),
         "seconds_measured": round(t4 - t0, 2), "seconds_extrapolated": round(t_total, 2),
+        "os_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
     }
 
 
@@ -355,6 +468,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
     }
+    if not args.no_extras:
+        print("# each step alone, warm and cold", file=sys.stderr, flush=True)
+        result["stages"] = stages(B, w, pr, sc, host, ka, va, kcs, vcs, buf)
+        result["sclk_mhz_after"] = sclk_mhz()
     if not args.no_extras and prior_kv:
         print("# split-phase attention and baseline modes", file=sys.stderr, flush=True)
         result["split_phase"] = split_phase(B, pr, host, ka, va, buf.k_pass, buf.v_pass, attn_ms)
