@@ -18,9 +18,10 @@ Extra objects (skipped with --no-extras):
   * `stages`: each step of the path alone on one stream (median and min of 20
     HIP-event timings, each behind a short spin kernel so that host overhead
     stays outside the events), warm and with the Infinity Cache evicted before
-    every rep, with its algorithmic bytes (or FLOPs) and fraction of the HBM (or bf16
-    MFMA) peak, and scoring + top-l + gather combined; `sclk_mhz_after` is the
-    shader clock rocm-smi reports right after;
+    every rep (by a 512 MB read; `cold_dirty` by a 512 MB write), with its
+    algorithmic bytes (or FLOPs) and fraction of the HBM (or bf16 MFMA) peak,
+    and scoring + top-l + gather combined; `sclk_mhz_after` is the shader
+    clock rocm-smi reports right after;
   * `split_phase`: anchor + local, then passing, then the merge of the two
     partial results (what lets the exchange between hosts overlap compute);
   * `modes`: the per-host attention of the two baselines the pages compare APB
@@ -138,16 +139,25 @@ def _stage_times(fn, reps: int, warm: int, evict=None):
 def stages(B, w, pr, sc, host, ka, va, kcs, vcs, buf, reps=20, warm=5):
     """Each step of the path alone on one stream: score (a1), top-l + gather (a2+a3),
     passing build (a5) and attention (a6).  Warm: inputs as the previous rep left the
-    caches.  Cold: a 512 MB buffer is written before every rep, outside the timed region,
-    which evicts the 256 MB Infinity Cache."""
+    caches.  Cold: a 512 MB buffer is read before every rep, outside the timed region,
+    which evicts the 256 MB Infinity Cache and leaves it clean.  Cold dirty: the 512 MB
+    buffer is written instead; the step then also pays for writing back the dirty lines."""
     import torch
     L, Hq, Hkv, d, l, hs = (w.local_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.pass_per_host,
                             w.hidden)
     g = Hq // Hkv
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    scratch = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    scratch_i = scratch.view(torch.int32)
+    total = torch.zeros((), dtype=torch.int64, device="cuda")
     fill = [0]
 
     def evict():
+        # reading 512 MB leaves the Infinity Cache full of clean lines
+        torch.sum(scratch_i, dim=0, out=total)
+
+    def evict_dirty():
+        # writing 512 MB leaves it full of dirty lines, whose write-back then
+        # competes with the step's own reads
         fill[0] = (fill[0] + 1) & 0xFF
         scratch.fill_(fill[0])
 
@@ -175,8 +185,10 @@ def stages(B, w, pr, sc, host, ka, va, kcs, vcs, buf, reps=20, warm=5):
         r = {"us_median": med * 1e3, "us_min": mn * 1e3}
         if name in byt:
             cmed, cmn = _stage_times(fn, reps, warm, evict=evict)
-            r.update({"cold_us_median": cmed * 1e3, "cold_us_min": cmn * 1e3, "bytes": byt[name],
-                      "gbs": byt[name] / (med * 1e-3) / 1e9, "cold_gbs": byt[name] / (cmed * 1e-3) / 1e9})
+            dmed, _ = _stage_times(fn, reps, warm, evict=evict_dirty)
+            r.update({"cold_us_median": cmed * 1e3, "cold_us_min": cmn * 1e3, "cold_dirty_us_median": dmed * 1e3,
+                      "bytes": byt[name], "gbs": byt[name] / (med * 1e-3) / 1e9,
+                      "cold_gbs": byt[name] / (cmed * 1e-3) / 1e9})
             r["frac_hbm_peak"] = r["gbs"] / PEAK_HBM_GBS
             r["cold_frac_hbm_peak"] = r["cold_gbs"] / PEAK_HBM_GBS
         else:
@@ -185,10 +197,10 @@ def stages(B, w, pr, sc, host, ka, va, kcs, vcs, buf, reps=20, warm=5):
                       / PEAK_BF16_TFLOPS})
         res[name] = r
     # scoring + top-l + gather together: their bytes over their summed time
-    for tag in ("", "cold_"):
+    for tag in ("", "cold_", "cold_dirty_"):
         t = res["a1_score"][tag + "us_median"] + res["a2a3_topl_gather"][tag + "us_median"]
         b = byt["a1_score"] + byt["a2a3_topl_gather"]
-        res[tag + "a1_a3"] = {"us_median": t, "gbs": b / (t * 1e-6) / 1e9,
+        res[(tag or "warm_") + "a1_a3"] = {"us_median": t, "gbs": b / (t * 1e-6) / 1e9,
                               "frac_hbm_peak": b / (t * 1e-6) / 1e9 / PEAK_HBM_GBS}
     del scratch
     return res
