@@ -21,7 +21,7 @@ Extra objects (skipped with --no-extras):
     every rep (by a 512 MB read; `cold_dirty` by a 512 MB write), with its
     algorithmic bytes (or FLOPs) and fraction of the HBM (or bf16 MFMA) peak,
     and scoring + top-l + gather combined; `sclk_mhz_after` is the shader
-    clock rocm-smi reports right after;
+    clock level the amdgpu driver reports right after;
   * `split_phase`: anchor + local, then passing, then the merge of the two
     partial results (what lets the exchange between hosts overlap compute);
   * `modes`: the per-host attention of the two baselines the pages compare APB
@@ -207,16 +207,22 @@ def stages(B, w, pr, sc, host, ka, va, kcs, vcs, buf, reps=20, warm=5):
 
 
 def sclk_mhz():
-    """Current shader clock of GPU 0 as rocm-smi reports it (MHz), or None."""
+    """Current shader clock level (MHz) from the amdgpu sysfs table of the first GPU that
+    has one (the level in use is marked '*'), or None.  Read from sysfs, not rocm-smi, so
+    that no child program starts."""
+    import glob
     import re
-    import subprocess
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
-                             timeout=20).stdout
-    except (OSError, subprocess.SubprocessError):
-        return None
-    m = re.search(r"sclk[^\n]*?\((\d+)\s*Mhz\)", out, re.IGNORECASE)
-    return int(m.group(1)) if m else None
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*mhz", line, re.IGNORECASE)
+                        if m:
+                            return int(m.group(1))
+        except OSError:
+            continue
+    return None
 
 
 def cpu_model():
