@@ -181,6 +181,37 @@ def test_topk_gather_near_equal_scores(L, l, spread):
     assert np.array_equal(from_device_bf16(kc), kr) and np.array_equal(from_device_bf16(vc), vr)
 
 
+@pytest.mark.parametrize("L,l,kind", [
+    (16384, 1024, "adversarial"), (16384, 1024, "quantized"), (25600, 1600, "quantized"),
+    (16384, 2048, "gaussian"), (4096, 100, "gaussian"), (16384, 1024, "gaussian"),
+])
+def test_topk_gather_structured_scores(L, l, kind):
+    """Bit-exact selection on structured scores.  adversarial: every 16th position holds
+    one of the 1024 largest scores (a regular stride that an estimate from evenly spaced
+    samples would get wrong).  quantized: scores on a coarse grid, so the l-th best
+    value is shared by ~100 keys and the tie rule picks the lowest indices among them.
+    gaussian: the l/L of the llama8b and qwen14b shapes, and L = 4096."""
+    Hkv, d = 2, 64
+    rng = np.random.default_rng(L + l)
+    s = rng.standard_normal((Hkv, L))
+    if kind == "adversarial":
+        s = -np.abs(s)
+        pos = (np.arange(1024) * L) // 1024
+        s[:, pos] = 1000.0 + np.arange(1024)[None, :]
+    elif kind == "quantized":
+        s = np.round(s * 20.0) / 20.0
+    s = s.astype(np.float32)
+    k = synth.random_bf16((L, Hkv, d), 14, stream=L)
+    v = synth.random_bf16((L, Hkv, d), 15, stream=L)
+    pr = B.Problem(Hkv, Hkv, d, L, 0, l, 1, 2, None)
+    idx, kc, vc = B.apb_topk_gather(pr, to_device_f32(s), to_device_bf16(k), to_device_bf16(v))
+    torch.cuda.synchronize()
+    idx_np = _np(idx)
+    assert np.array_equal(idx_np, orc.topl(s, l))
+    kr, vr = orc.gather(k, v, idx_np)
+    assert np.array_equal(from_device_bf16(kc), kr) and np.array_equal(from_device_bf16(vc), vr)
+
+
 def test_host_step_on_two_streams_matches_one_stream():
     """Compression on a side stream beside the attention: identical bits to one stream."""
     w = synth.Workload("two_streams", 208, 3, 300, 40, 50, 4, 2, 128, 64, 1.0, 2)
