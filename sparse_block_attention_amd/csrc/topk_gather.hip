@@ -64,7 +64,7 @@ constexpr int kBatch = 8;
 
 template <bool KEYS_IN_LDS>
 __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const TopkArgs a) {
-  __shared__ uint32_t keys[KEYS_IN_LDS ? kLdsKeys : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t keys[KEYS_IN_LDS ? kLdsKeys : 1];
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t wtot[2][kTopkWaves];
   __shared__ uint32_t sel_digit, sel_greater;
@@ -179,6 +179,62 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const TopkArg
   const uint32_t need = (uint32_t)k_rem;       // elements == T to keep, >= 1
 
   // (common == 32: every key equals kmin, which is T)
+  int32_t *out = a.idx + (size_t)h * a.l;
+  const uint32_t l = (uint32_t)a.l;
+  if constexpr (KEYS_IN_LDS) {
+    // 2. stable compaction, keys in LDS: thread t owns the run of `per` consecutive
+    // indices starting at t*per (per a multiple of 4, so each run is read with
+    // 16-byte loads into registers); one block-wide scan of the per-thread counts
+    // of keys > T and == T gives every thread its output positions.
+    constexpr int kMaxPer = kLdsKeys / kTopkThreads;   // 32
+    const int per = (((L + kTopkThreads - 1) / kTopkThreads) + 3) & ~3;
+    const int b = tid * per;
+    uint32_t kr[kMaxPer];
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; j += 4) {
+      if (j < per) {
+        const uint4 q4 = *reinterpret_cast<const uint4 *>(&keys[b + j]);
+        kr[j] = q4.x;
+        kr[j + 1] = q4.y;
+        kr[j + 2] = q4.z;
+        kr[j + 3] = q4.w;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool in = b + j + u < L;
+          ngt += (in && kr[j + u] > T) ? 1u : 0u;
+          neq += (in && kr[j + u] == T) ? 1u : 0u;
+        }
+      }
+    }
+    const uint32_t ig = wave_inclusive_scan(ngt, lane);
+    const uint32_t ie = wave_inclusive_scan(neq, lane);
+    if (lane == 63) {
+      wtot[0][wave] = ig;
+      wtot[1][wave] = ie;
+    }
+    __syncthreads();
+    uint32_t g = ig - ngt, e = ie - neq;            // keys > T and == T before this run
+    for (int w = 0; w < wave; ++w) {
+      g += wtot[0][w];
+      e += wtot[1][w];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      if (j < per && b + j < L) {
+        const uint32_t kk = kr[j];
+        if (kk > T) {
+          const uint32_t pos = g + min(e, need);
+          if (pos < l) out[pos] = b + j;
+          ++g;
+        } else if (kk == T) {
+          if (e < need && g + e < l) out[g + e] = b + j;
+          ++e;
+        }
+      }
+    }
+    return;
+  }
   // 2. stable compaction: wave w owns indices [w*C, (w+1)*C), C a multiple of 64
   const int C = ((L + kTopkThreads - 1) / kTopkThreads) * 64;
   const int lo = min(wave * C, L);
@@ -212,8 +268,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const TopkArg
     g_before += wtot[0][w];
     e_before += wtot[1][w];
   }
-  int32_t *out = a.idx + (size_t)h * a.l;
-  const uint32_t l = (uint32_t)a.l;
   for_each_run_key([&](int i, uint32_t kk, bool valid) {
     const bool gt = valid && kk > T;
     const bool eq = valid && kk == T;
