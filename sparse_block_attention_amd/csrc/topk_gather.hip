@@ -13,11 +13,15 @@
 //     Each pass keeps only the keys whose higher digits match the digits chosen
 //     so far; a suffix scan over the bins (largest digit first) finds the digit
 //     of the l-th best key.  The result is the key T of the l-th best element
-//     and how many elements equal to T are still needed (`need`).
+//     and how many elements equal to T are still needed (`need`).  When the
+//     chosen bin holds exactly the keys still needed, all of them are kept and
+//     the lower digits are skipped: T is the bin's lowest key and every key
+//     >= T is kept.
 //  2. a stable compaction in index order keeps every key > T and the first
-//     `need` keys == T.  Each wave owns a contiguous run of indices; ballots
-//     and lane-mask bit counts give each kept element its output position, so
-//     the result does not depend on timing.
+//     `need` keys == T.  With keys in LDS each thread owns a run of consecutive
+//     indices and one block scan of its counts places its kept keys; above
+//     that, each wave owns a contiguous run and ballots plus lane-mask bit
+//     counts place them.  Either way the result does not depend on timing.
 // gfx950 design: one 1024-thread workgroup (16 wave64s) per kv head.  Keys stay
 // in LDS (128 KB) when the block has at most 32768 tokens; otherwise every pass
 // re-reads the fp32 scores, which stay in L2 (512 KB per head at 131072
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const TopkArg
   __shared__ __attribute__((aligned(16))) uint32_t keys[KEYS_IN_LDS ? kLdsKeys : 1];
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t wtot[2][kTopkWaves];
-  __shared__ uint32_t sel_digit, sel_greater;
+  __shared__ uint32_t sel_digit, sel_greater, sel_count;
 
   const int h = blockIdx.x;
   const int tid = threadIdx.x;
@@ -100,11 +104,38 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const TopkArg
   // leading bits of the smallest and the largest key.  They need no pass; the
   // first digit starts below them.
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for_each_key(true, [&](int i, uint32_t kk) {
-    if constexpr (KEYS_IN_LDS) keys[i] = kk;
-    kmin = min(kmin, kk);
-    kmax = max(kmax, kk);
-  });
+  bool loaded = false;
+  if constexpr (KEYS_IN_LDS) {
+    static_assert(kLdsKeys / 4 <= kBatch * kTopkThreads, "one batch of 16-byte loads");
+    if ((L & 3) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0) {
+      // rows start 16-byte aligned: 16-byte loads, all of a thread's in one batch
+      // (at most 32768 / 4 / 1024 = 8 per thread)
+      const int n4 = L >> 2;
+      const float4 *s4 = reinterpret_cast<const float4 *>(srow);
+      float4 fb[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) fb[j] = s4[min(j * kTopkThreads + tid, n4 - 1)];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i4 = j * kTopkThreads + tid;
+        if (i4 < n4) {
+          const uint4 kq = make_uint4(order_key(fb[j].x), order_key(fb[j].y), order_key(fb[j].z),
+                                      order_key(fb[j].w));
+          *reinterpret_cast<uint4 *>(&keys[4 * i4]) = kq;
+          kmin = min(kmin, min(min(kq.x, kq.y), min(kq.z, kq.w)));
+          kmax = max(kmax, max(max(kq.x, kq.y), max(kq.z, kq.w)));
+        }
+      }
+      loaded = true;
+    }
+  }
+  if (!loaded) {
+    for_each_key(true, [&](int i, uint32_t kk) {
+      if constexpr (KEYS_IN_LDS) keys[i] = kk;
+      kmin = min(kmin, kk);
+      kmax = max(kmax, kk);
+    });
+  }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor(kmin, d, 64));
@@ -130,6 +161,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const TopkArg
   uint32_t mask = common == 32 ? 0xffffffffu : (common ? ~0u << (32 - common) : 0u);
   int k_rem = a.l;
   int low = 32 - common;                        // bits still to resolve: [low-1 .. 0]
+  bool take_all_eq = false;
 #pragma unroll 1
   while (low > 0) {
     const int width = low < 12 ? low : 12;
@@ -165,6 +197,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const TopkArg
         if (acc + c[j] >= (uint32_t)k_rem) {
           sel_digit = (uint32_t)(kBins - 1 - (4 * tid + j));
           sel_greater = acc;
+          sel_count = c[j];
           break;
         }
         acc += c[j];
@@ -174,9 +207,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const TopkArg
     prefix |= sel_digit << shift;
     mask |= dmask << shift;
     k_rem -= (int)sel_greater;
+    // Every key of the chosen bin is kept when the bin holds exactly the keys still
+    // needed: then the kept set is {key >= prefix} whatever the lower bits, and the
+    // remaining digits are skipped (prefix has zeros below the resolved bits).
+    if (sel_count == (uint32_t)k_rem) {
+      take_all_eq = true;
+      break;
+    }
   }
   const uint32_t T = prefix;
-  const uint32_t need = (uint32_t)k_rem;       // elements == T to keep, >= 1
+  // elements == T to keep, >= 1 (all of them after an early exit: keys > T and == T
+  // are then both kept, at positions counting both)
+  const uint32_t need = take_all_eq ? 0xffffffffu : (uint32_t)k_rem;
 
   // (common == 32: every key equals kmin, which is T)
   int32_t *out = a.idx + (size_t)h * a.l;

@@ -184,13 +184,17 @@ def test_topk_gather_near_equal_scores(L, l, spread):
 @pytest.mark.parametrize("L,l,kind", [
     (16384, 1024, "adversarial"), (16384, 1024, "quantized"), (25600, 1600, "quantized"),
     (16384, 2048, "gaussian"), (4096, 100, "gaussian"), (16384, 1024, "gaussian"),
+    (16384, 1024, "one_bin"), (5000, 300, "one_bin_ties"),
 ])
 def test_topk_gather_structured_scores(L, l, kind):
     """Bit-exact selection on structured scores.  adversarial: every 16th position holds
     one of the 1024 largest scores (a regular stride that an estimate from evenly spaced
     samples would get wrong).  quantized: scores on a coarse grid, so the l-th best
     value is shared by ~100 keys and the tie rule picks the lowest indices among them.
-    gaussian: the l/L of the llama8b and qwen14b shapes, and L = 4096."""
+    gaussian: the l/L of the llama8b and qwen14b shapes, and L = 4096.  one_bin(_ties):
+    the l best scores lie in [1, 1.125) (one sign/exponent/3-mantissa-bit bin) and every
+    other score is negative, so the first digit already holds exactly the l keys needed;
+    distinct values there, or 7 tied values."""
     Hkv, d = 2, 64
     rng = np.random.default_rng(L + l)
     s = rng.standard_normal((Hkv, L))
@@ -200,6 +204,11 @@ def test_topk_gather_structured_scores(L, l, kind):
         s[:, pos] = 1000.0 + np.arange(1024)[None, :]
     elif kind == "quantized":
         s = np.round(s * 20.0) / 20.0
+    elif kind in ("one_bin", "one_bin_ties"):
+        s = -np.abs(s) - 0.01
+        vals = 1.0 + (np.arange(l) / (8.0 * l) if kind == "one_bin" else (np.arange(l) % 7) / 64.0)
+        for h in range(Hkv):
+            s[h, rng.choice(L, size=l, replace=False)] = rng.permutation(vals)
     s = s.astype(np.float32)
     k = synth.random_bf16((L, Hkv, d), 14, stream=L)
     v = synth.random_bf16((L, Hkv, d), 15, stream=L)
