@@ -23,7 +23,8 @@
 //    sit in LDS in a permuted slot order chosen so that lane half h of the
 //    accumulator holds keys 16h..16h+15 of the block, in order; those values,
 //    converted to bf16, are directly the B operand of O^T = V^T P^T (no lane
-//    movement of P).  16-byte chunks of a K row are XOR-swizzled by the slot.
+//    movement of P).  K rows are padded to an odd number of 16-byte chunks, so
+//    the reads are conflict-free with the head-dim offset as an immediate.
 //  * V stays row-major in LDS (32-byte granules XOR-swizzled by key) and the A
 //    operand of O^T = V^T P^T is read with ds_read_b64_tr_b16, which transposes
 //    4 keys x 16 head-dim values across each 16-lane group.
@@ -102,28 +103,35 @@ template <int D, int NSUB, int BN, int NW>
 struct AttnCfg {
   static constexpr int kThreads = 64 * NW;
   static constexpr int BM = NW * 32 * NSUB;      // query rows per workgroup
-  static constexpr int ROWB = D * 2;             // bytes per K/V row in LDS (no padding)
-  static constexpr int TILE_BYTES = BN * ROWB;   // one K or V tile
+  static constexpr int ROWB = D * 2;             // bytes per V row in LDS (no padding)
+  static constexpr int TILE_BYTES = BN * ROWB;   // one V tile
+  static constexpr int KROWB = ROWB + 16;        // bytes per K row in LDS: one 16-byte pad
+  static constexpr int KTB = BN * KROWB;         // one K tile
+  static constexpr int SB = KTB + TILE_BYTES;    // one LDS buffer: K tile, then V tile
   static constexpr int CH = D / 8;               // 16-byte chunks per row
   static constexpr int GR = D / 16;              // 32-byte granules per row
-  static constexpr int KI = TILE_BYTES / 1024 / NW;  // 1 KB LDS-DMA loads per wave per tile
+  static constexpr int KI = TILE_BYTES / 1024 / NW;  // 1 KB LDS-DMA loads of V per wave per tile
+  static constexpr int NKL = KTB / 1024;             // 1 KB LDS-DMA loads of one K tile
+  static constexpr int KIK = (NKL + NW - 1) / NW;    // K loads per wave (the last ones: low waves only)
   static constexpr int NKB = BN / 32;            // 32-key blocks per tile
   static constexpr int DB = D / 32;              // 32-wide head-dim blocks of O
   static constexpr int KK = D / 16;              // MFMA k-steps over head_dim
   static_assert(KI >= 1 && KI * 1024 * NW == TILE_BYTES, "tile split over LDS-DMA loads");
+  static_assert(NKL * 1024 == KTB && SB % 1024 == 0, "padded K tile split over LDS-DMA loads");
 };
 
 // V tile granule swizzle: 32-byte granule g of key row `key` sits at g ^ vsw(key).
 template <int GR>
 __device__ __forceinline__ int vsw(int key) { return (2 * (key & 3)) & (GR - 1); }
 
-// Issue this wave's LDS-DMA loads of one K tile and one V tile (KI x 1 KB each).
-// The buffer descriptors cover rows [k0, seg_len) of the segment (at most BN), so
-// rows past a segment's end read as zeros.  (The body exists only in the device
-// pass: the host pass has no buffer-descriptor type.)
-template <int KI, int BN>
-__device__ __forceinline__ void issue_tile_loads(const TileRef &t, int kv_row_bytes, uint8_t *kdst, uint8_t *vdst,
-                                                 const int (&koff)[KI], const int (&voff)[KI]) {
+// Issue this wave's LDS-DMA loads of one K tile (loads wave, wave + NW, ... of the
+// NKL 1 KB pieces) and one V tile (KI x 1 KB).  The buffer descriptors cover rows
+// [k0, seg_len) of the segment (at most BN), so rows past a segment's end read as
+// zeros.  (The body exists only in the device pass: the host pass has no
+// buffer-descriptor type.)
+template <int KI, int KIK, int NKL, int NW, int BN>
+__device__ __forceinline__ void issue_tile_loads(const TileRef &t, int kv_row_bytes, int wave, uint8_t *kdst,
+                                                 uint8_t *vdst, const int (&koff)[KIK], const int (&voff)[KI]) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const int valid_bytes = min(t.seg_len - t.k0, BN) * kv_row_bytes;
   const size_t base = (size_t)t.k0 * (size_t)(kv_row_bytes / 2);
@@ -132,10 +140,13 @@ __device__ __forceinline__ void issue_tile_loads(const TileRef &t, int kv_row_by
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc((void *)(t.v + base), 0, valid_bytes, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < KI; ++i) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(kdst + i * 1024), 16, koff[i], 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vdst + i * 1024), 16, voff[i], 0, 0, 0);
+  for (int i = 0; i < KIK; ++i) {
+    if (i * NW + NW <= NKL || i * NW + wave < NKL)  // wave-uniform
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(kdst + i * NW * 1024), 16, koff[i], 0, 0, 0);
   }
+#pragma unroll
+  for (int i = 0; i < KI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(vdst + i * 1024), 16, voff[i], 0, 0, 0);
 #endif
 }
 
@@ -146,12 +157,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, 8)
 void block_attention_kernel(const AttnArgs a) {
   using C = AttnCfg<D, NSUB, BN, NW>;
   constexpr int BM = C::BM, ROWB = C::ROWB, TB = C::TILE_BYTES, CH = C::CH, GR = C::GR, KI = C::KI;
+  constexpr int KROWB = C::KROWB, KTB = C::KTB, SB = C::SB, KIK = C::KIK, NKL = C::NKL;
   constexpr int NKB = C::NKB, DB = C::DB, KK = C::KK;
 
   // [buffer][K tile | V tile]; tile t uses buffer t % NBUF and tile t + PD is in
   // flight while tile t is consumed.
   constexpr int PD = APB_ATTN_PD, NBUF = PD + 1;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * 2 * TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * SB];
 
   // ---- work item: XCD-aware remap, then (kv head, q tile longest-first, member)
   const int nb = gridDim.x;
@@ -175,7 +187,7 @@ void block_attention_kernel(const AttnArgs a) {
   const int kv_row_bytes = a.Hkv * D * 2;
 
   // ---- zero both LDS buffers once: rows past a segment end never hold NaN
-  for (int i = tid; i < NBUF * 2 * TB / 16; i += C::kThreads) reinterpret_cast<uint4 *>(smem)[i] = uint4{0, 0, 0, 0};
+  for (int i = tid; i < NBUF * SB / 16; i += C::kThreads) reinterpret_cast<uint4 *>(smem)[i] = uint4{0, 0, 0, 0};
 
   // ---- Q fragments (B operand of S^T = K Q^T): row lrow, head-dim 16kk + 8half..+7
   bf16x8 qf[NSUB][KK];
@@ -193,16 +205,24 @@ void block_attention_kernel(const AttnArgs a) {
   }
 
   // ---- per-lane source offsets of the LDS-DMA loads (fixed for the whole kernel).
-  // Load i of this wave fills LDS bytes [(wave*KI + i) * 1024, +1024) of a tile;
-  // lane p writes 16 bytes at p*16 of that range.
-  int koff[KI], voff[KI];
+  // Lane p of a load writes 16 bytes at p*16 of the load's 1 KB.  K load i of this
+  // wave fills bytes [(i*NW + wave) * 1024, +1024) of the padded K tile: LDS row
+  // `row` (KROWB bytes) is slot `row`, holding key slot_key(row), chunks in order,
+  // then a pad (filled with a copy of the last chunk).  V load i fills bytes
+  // [(wave*KI + i) * 1024, +1024) of the V tile.
+  int koff[KIK], voff[KI];
+#pragma unroll
+  for (int i = 0; i < KIK; ++i) {
+    const int pos = (i * NW + wave) * 64 + lane;  // 16-byte position in the padded K tile
+    const int row = min(pos / (CH + 1), BN - 1);   // (rows past BN: a load that is never issued)
+    const int pc = min(pos % (CH + 1), CH - 1);
+    koff[i] = slot_key(row) * kv_row_bytes + h * D * 2 + pc * 16;
+  }
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
-    const int pos = (wave * KI + i) * 64 + lane;  // 16-byte position in the tile
+    const int pos = (wave * KI + i) * 64 + lane;  // 16-byte position in the V tile
     const int row = pos / CH;
     const int pc = pos % CH;
-    // K: LDS row `row` is slot `row`, holding key slot_key(row); chunk pc holds chunk pc ^ (row % CH).
-    koff[i] = slot_key(row) * kv_row_bytes + h * D * 2 + ((pc ^ (row & (CH - 1))) * 16);
     // V: LDS row = key; granule pc/2 holds granule (pc/2) ^ vsw(key).
     const int gi = (pc >> 1) ^ vsw<GR>(row);
     voff[i] = row * kv_row_bytes + h * D * 2 + (gi * 2 + (pc & 1)) * 16;
@@ -233,9 +253,11 @@ void block_attention_kernel(const AttnArgs a) {
   };
 
   // ---- per-lane LDS read offsets
-  // K (A operand of S^T): slot kb*32 + lrow, chunk (2kk + half) ^ (lrow % CH)
-  const int k_rd = lrow * ROWB;
-  const int k_x = lrow & (CH - 1);
+  // K (A operand of S^T): slot kb*32 + lrow, chunk 2kk + half.  The padded row
+  // stride is an odd number of 16-byte chunks, so 16 consecutive slots start on 16
+  // distinct 16-byte bank groups (64 banks x 4 bytes) and the reads are
+  // conflict-free; kb and kk then enter the address as immediate offsets.
+  const int k_rd = lrow * KROWB + half * 16;
   // V (A operand of O^T via the transposing read): 16-lane group gq reads keys
   // base + (lane%16)/4 at head-dim db*32 + (gq%2)*16 + 4*(lane%4) .. +3.
   const int gq = lane >> 4;
@@ -267,8 +289,9 @@ void block_attention_kernel(const AttnArgs a) {
   // ---- prologue
   __syncthreads();  // LDS zeroed before the first DMA lands
   for (int j = 0; j < PD && j < n_tiles; ++j) {
-    uint8_t *kdst = smem + j * 2 * TB + wave * KI * 1024;
-    issue_tile_loads<KI, BN>(tile_ref(j), kv_row_bytes, kdst, kdst + TB, koff, voff);
+    uint8_t *dst = smem + j * SB;
+    issue_tile_loads<KI, KIK, NKL, NW, BN>(tile_ref(j), kv_row_bytes, wave, dst + wave * 1024,
+                                           dst + KTB + wave * KI * 1024, koff, voff);
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -280,12 +303,12 @@ void block_attention_kernel(const AttnArgs a) {
   auto tile_step = [&](int t, const uint8_t *__restrict__ cur_buf, uint8_t *__restrict__ nxt, bool prefetch) {
     const TileRef cur = tile_ref(t);
     if (prefetch) {
-      uint8_t *kdst = nxt + wave * KI * 1024;
-      issue_tile_loads<KI, BN>(tile_ref(t + PD), kv_row_bytes, kdst, kdst + TB, koff, voff);
+      issue_tile_loads<KI, KIK, NKL, NW, BN>(tile_ref(t + PD), kv_row_bytes, wave, nxt + wave * 1024,
+                                             nxt + KTB + wave * KI * 1024, koff, voff);
     }
 
     const uint8_t *Ks = cur_buf;
-    const uint8_t *Vs = cur_buf + TB;
+    const uint8_t *Vs = cur_buf + KTB;
     const bool wave_active = !(cur.seg == 2 && cur.k0 > rw + 32 * NSUB - 1);
     if (wave_active) {
       // S^T = K Q^T, one 32-key block at a time
@@ -294,14 +317,20 @@ void block_attention_kernel(const AttnArgs a) {
       for (int s = 0; s < NSUB; ++s)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) sacc[s][kb] = f32x16{};
+      // K fragments of block kb+1 are read into the slots that block kb has used,
+      // so KK reads are in flight ahead of the MFMAs.
+      const uint8_t *kr = Ks + k_rd;
+      bf16x8 kf[KK];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kf[kk] = *reinterpret_cast<const bf16x8 *>(kr + kk * 32);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + kb * 32 * ROWB + k_rd + (((2 * kk + half) ^ k_x) * 16));
 #pragma unroll
           for (int s = 0; s < NSUB; ++s)
-            sacc[s][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s][kk], sacc[s][kb], 0, 0, 0);
+            sacc[s][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[s][kk], sacc[s][kb], 0, 0, 0);
+          if (kb + 1 < NKB) kf[kk] = *reinterpret_cast<const bf16x8 *>(kr + (kb + 1) * 32 * KROWB + kk * 32);
         }
       }
 #if APB_ATTN_SCHED
@@ -407,11 +436,12 @@ void block_attention_kernel(const AttnArgs a) {
   for (int t = 0; t < n_tiles; ++t) {
     const bool prefetch = t + PD < n_tiles;
     const int pb = (buf + PD >= NBUF) ? buf + PD - NBUF : buf + PD;
-    tile_step(t, smem + buf * 2 * TB, smem + pb * 2 * TB, prefetch);
+    tile_step(t, smem + buf * SB, smem + pb * SB, prefetch);
 
     // Tile t+1 must have landed in every wave before the barrier; the loads of
-    // tiles t+2 .. t+PD (2*KI per tile and wave) may stay in flight across it.
-    if (prefetch) wait_vmcnt<2 * KI * (PD - 1)>();
+    // tiles t+2 .. t+PD (at least KI + NKL/NW per tile and wave) may stay in
+    // flight across it.
+    if (prefetch) wait_vmcnt<(KI + NKL / NW) * (PD - 1)>();
     else wait_vmcnt<0>();
     barrier_keep_dma();
     buf = (buf + 1 == NBUF) ? 0 : buf + 1;
