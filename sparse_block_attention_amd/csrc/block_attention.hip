@@ -296,7 +296,6 @@ void block_attention_kernel(const AttnArgs a) {
   wait_vmcnt<0>();
   __syncthreads();
 
-  int buf = 0;  // t % NBUF
   // One tile: prefetch tile t+PD into `nxt`, consume tile t from `cur`.  The two
   // buffers are distinct; saying so (__restrict__) lets the compiler skip the
   // wait for the in-flight DMA before reading `cur`.
@@ -364,7 +363,7 @@ void block_attention_kernel(const AttnArgs a) {
         // is too large (or not finite, as on the first tile) moves the reference to
         // the true max, rescales O and the sum, and recomputes.
         auto exp_tile = [&](float m_use) {
-          float psum = 0.f;
+          float psum;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -374,7 +373,7 @@ void block_attention_kernel(const AttnArgs a) {
               for (int j = 0; j < 4; ++j) {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s][kb][c * 8 + 2 * j], sl2, -m_use));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s][kb][c * 8 + 2 * j + 1], sl2, -m_use));
-                psum += p0 + p1;
+                psum = (kb == 0 && c == 0 && j == 0) ? p0 + p1 : psum + (p0 + p1);
                 w4[j] = bf16x2_bits(p0, p1);
               }
               pf[s][kb][c] = __builtin_bit_cast(bf16x8, (uint4{w4[0], w4[1], w4[2], w4[3]}));
@@ -433,18 +432,38 @@ void block_attention_kernel(const AttnArgs a) {
     }
   };
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const bool prefetch = t + PD < n_tiles;
-    const int pb = (buf + PD >= NBUF) ? buf + PD - NBUF : buf + PD;
-    tile_step(t, smem + buf * SB, smem + pb * SB, prefetch);
-
-    // Tile t+1 must have landed in every wave before the barrier; the loads of
-    // tiles t+2 .. t+PD (at least KI + NKL/NW per tile and wave) may stay in
-    // flight across it.
+  // Tile t+1 must have landed in every wave before the barrier that ends tile t;
+  // the loads of tiles t+2 .. t+PD (at least KI + NKL/NW per tile and wave) may
+  // stay in flight across it.
+  auto tile_end = [&](bool prefetch) {
     if (prefetch) wait_vmcnt<(KI + NKL / NW) * (PD - 1)>();
     else wait_vmcnt<0>();
     barrier_keep_dma();
-    buf = (buf + 1 == NBUF) ? 0 : buf + 1;
+  };
+  if constexpr (NBUF == 2) {
+    // Two tiles per iteration, so that each one's buffers are constants and the
+    // LDS read addresses need no per-tile add.
+    int t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+      tile_step(t, smem, smem + SB, true);
+      tile_end(true);
+      const bool more = t + 2 < n_tiles;
+      tile_step(t + 1, smem + SB, smem, more);
+      tile_end(more);
+    }
+    if (t < n_tiles) {
+      tile_step(t, smem, smem + SB, false);
+      tile_end(false);
+    }
+  } else {
+    int buf = 0;  // t % NBUF
+    for (int t = 0; t < n_tiles; ++t) {
+      const bool prefetch = t + PD < n_tiles;
+      const int pb = (buf + PD >= NBUF) ? buf + PD - NBUF : buf + PD;
+      tile_step(t, smem + buf * SB, smem + pb * SB, prefetch);
+      tile_end(prefetch);
+      buf = (buf + 1 == NBUF) ? 0 : buf + 1;
+    }
   }
 
   // ---- epilogue: normalise, write O (bf16) and LSE (natural log)
