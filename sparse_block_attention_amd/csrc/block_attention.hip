@@ -177,7 +177,7 @@ void block_attention_kernel(const AttnArgs a) {
   const int qhead = a.qhead_of_slot[h * a.g + rem % a.g];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS targets stay scalar
   const int lane = tid & 63;
   const int lrow = lane & 31;
   const int half = lane >> 5;
