@@ -14,9 +14,9 @@
 //  * K/V tiles of BN keys go HBM -> LDS by LDS-DMA (buffer_load_dwordx4 ... lds):
 //    no staging registers, no LDS store instructions, and per-lane source offsets
 //    fixed for the whole kernel.  A per-tile buffer descriptor ends at the
-//    segment's last row, so rows past it read as zeros.  PD+1 LDS buffers: tiles
-//    t+1..t+PD are in flight while tile t is consumed (the DMA has PD tiles of
-//    compute to land); one barrier per tile.  Segment tails and
+//    segment's last row, so rows past it read as zeros.  Two LDS buffers: tile
+//    t+1 is in flight while tile t is consumed (the DMA has one tile of compute
+//    to land); one barrier per tile.  Segment tails and
 //    the causal diagonal are masked; local tiles past a wave's rows are skipped.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the query row is the MFMA column,
 //    so each lane holds the scores of one row (16 keys per 32-key block).  K rows
@@ -48,9 +48,6 @@
 #endif
 #ifndef APB_ATTN_WPE
 #define APB_ATTN_WPE 2
-#endif
-#ifndef APB_ATTN_PD
-#define APB_ATTN_PD 1
 #endif
 #ifndef APB_ATTN_SCHED
 #define APB_ATTN_SCHED 1
@@ -85,9 +82,11 @@ __device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
+// One K/V tile: its segment (0 anchor, 1 passing, 2 local), its first key k0
+// within the segment, the segment length, and K/V pointers at row k0.
 struct TileRef {
   const uint16_t *k, *v;
-  int k0, seg_len, seg;  // seg: 0 anchor, 1 passing, 2 local
+  int k0, seg_len, seg;
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -134,11 +133,8 @@ __device__ __forceinline__ void issue_tile_loads(const TileRef &t, int kv_row_by
                                                  uint8_t *vdst, const int (&koff)[KIK], const int (&voff)[KI]) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const int valid_bytes = min(t.seg_len - t.k0, BN) * kv_row_bytes;
-  const size_t base = (size_t)t.k0 * (size_t)(kv_row_bytes / 2);
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(t.k + base), 0, valid_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(t.v + base), 0, valid_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)t.k, 0, valid_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)t.v, 0, valid_bytes, 0x00020000);
 #pragma unroll
   for (int i = 0; i < KIK; ++i) {
     if (i * NW + NW <= NKL || i * NW + wave < NKL)  // wave-uniform
@@ -160,9 +156,9 @@ void block_attention_kernel(const AttnArgs a) {
   constexpr int KROWB = C::KROWB, KTB = C::KTB, SB = C::SB, KIK = C::KIK, NKL = C::NKL;
   constexpr int NKB = C::NKB, DB = C::DB, KK = C::KK;
 
-  // [buffer][K tile | V tile]; tile t uses buffer t % NBUF and tile t + PD is in
+  // [buffer][K tile | V tile]; tile t uses buffer t % 2 and tile t + 1 is in
   // flight while tile t is consumed.
-  constexpr int PD = APB_ATTN_PD, NBUF = PD + 1;
+  constexpr int NBUF = 2;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * SB];
 
   // ---- work item: XCD-aware remap, then (kv head, q tile longest-first, member)
@@ -235,21 +231,26 @@ void block_attention_kernel(const AttnArgs a) {
   const int nL = a.use_local ? (last_row + BN - 1) / BN : 0;
   const int n_tiles = nA + nP + nL;
 
-  // Segment pointers and lengths are read from the arguments once, here; the
-  // per-tile choice is then a scalar select rather than a fresh argument load
-  // (and its wait) at the top of every tile.
-  const uint16_t *const seg_k[3] = {a.ka, a.kp, a.kl};
-  const uint16_t *const seg_v[3] = {a.va, a.vp, a.vl};
-  const int seg_n[3] = {a.A, a.P, a.L};
-  auto tile_ref = [&](int t) {
-    TileRef r;
-    const int sg = t < nA ? 0 : (t < nA + nP ? 1 : 2);
-    r.seg = sg;
-    r.k = sg == 0 ? seg_k[0] : (sg == 1 ? seg_k[1] : seg_k[2]);
-    r.v = sg == 0 ? seg_v[0] : (sg == 1 ? seg_v[1] : seg_v[2]);
-    r.seg_len = sg == 0 ? seg_n[0] : (sg == 1 ? seg_n[1] : seg_n[2]);
-    r.k0 = (t - (sg == 0 ? 0 : (sg == 1 ? nA : nA + nP))) * BN;
-    return r;
+  // Tiles are walked by a cursor: the next tile is the current one advanced by BN
+  // rows, or the first tile of the next non-empty segment.  The segment pointers
+  // and lengths are read from the arguments here, before the loop, and the empty
+  // asm makes them live in registers from this point: a kernel-argument load left
+  // for the rare segment switch would be outstanding at the loop's first LDS waits.
+  const uint16_t *kp = a.kp, *vp = a.vp, *kl = a.kl, *vl = a.vl;
+  asm volatile("" : "+s"(kp), "+s"(vp), "+s"(kl), "+s"(vl));
+  const int seg_P = a.P, seg_L = a.L;
+  const int tile_elems = BN * (kv_row_bytes / 2);
+  TileRef first;
+  if (a.A > 0) first = TileRef{a.ka, a.va, 0, a.A, 0};
+  else if (seg_P > 0) first = TileRef{kp, vp, 0, seg_P, 1};
+  else first = TileRef{kl, vl, 0, seg_L, 2};
+  auto advance = [&](const TileRef &c) {
+    TileRef n{c.k + tile_elems, c.v + tile_elems, c.k0 + BN, c.seg_len, c.seg};
+    if (c.seg < 2 && n.k0 >= c.seg_len) {  // wave-uniform, once per segment
+      if (c.seg == 0 && seg_P > 0) n = TileRef{kp, vp, 0, seg_P, 1};
+      else n = TileRef{kl, vl, 0, seg_L, 2};
+    }
+    return n;
   };
 
   // ---- per-lane LDS read offsets
@@ -288,21 +289,19 @@ void block_attention_kernel(const AttnArgs a) {
 
   // ---- prologue
   __syncthreads();  // LDS zeroed before the first DMA lands
-  for (int j = 0; j < PD && j < n_tiles; ++j) {
-    uint8_t *dst = smem + j * SB;
-    issue_tile_loads<KI, KIK, NKL, NW, BN>(tile_ref(j), kv_row_bytes, wave, dst + wave * 1024,
-                                           dst + KTB + wave * KI * 1024, koff, voff);
-  }
+  if (n_tiles > 0)
+    issue_tile_loads<KI, KIK, NKL, NW, BN>(first, kv_row_bytes, wave, smem + wave * 1024,
+                                           smem + KTB + wave * KI * 1024, koff, voff);
   wait_vmcnt<0>();
   __syncthreads();
 
-  // One tile: prefetch tile t+PD into `nxt`, consume tile t from `cur`.  The two
+  // One tile: prefetch tile `nx` into `nxt`, consume tile `cur` from `cur_buf`.  The two
   // buffers are distinct; saying so (__restrict__) lets the compiler skip the
   // wait for the in-flight DMA before reading `cur`.
-  auto tile_step = [&](int t, const uint8_t *__restrict__ cur_buf, uint8_t *__restrict__ nxt, bool prefetch) {
-    const TileRef cur = tile_ref(t);
+  auto tile_step = [&](const TileRef &cur, const TileRef &nx, const uint8_t *__restrict__ cur_buf,
+                       uint8_t *__restrict__ nxt, bool prefetch) {
     if (prefetch) {
-      issue_tile_loads<KI, KIK, NKL, NW, BN>(tile_ref(t + PD), kv_row_bytes, wave, nxt + wave * 1024,
+      issue_tile_loads<KI, KIK, NKL, NW, BN>(nx, kv_row_bytes, wave, nxt + wave * 1024,
                                              nxt + KTB + wave * KI * 1024, koff, voff);
     }
 
@@ -432,38 +431,28 @@ void block_attention_kernel(const AttnArgs a) {
     }
   };
 
-  // Tile t+1 must have landed in every wave before the barrier that ends tile t;
-  // the loads of tiles t+2 .. t+PD (at least KI + NKL/NW per tile and wave) may
-  // stay in flight across it.
-  auto tile_end = [&](bool prefetch) {
-    if (prefetch) wait_vmcnt<(KI + NKL / NW) * (PD - 1)>();
-    else wait_vmcnt<0>();
+  // Tile t+1 must have landed in every wave before the barrier that ends tile t.
+  auto tile_end = [&]() {
+    wait_vmcnt<0>();
     barrier_keep_dma();
   };
-  if constexpr (NBUF == 2) {
-    // Two tiles per iteration, so that each one's buffers are constants and the
-    // LDS read addresses need no per-tile add.
-    int t = 0;
-    for (; t + 1 < n_tiles; t += 2) {
-      tile_step(t, smem, smem + SB, true);
-      tile_end(true);
-      const bool more = t + 2 < n_tiles;
-      tile_step(t + 1, smem + SB, smem, more);
-      tile_end(more);
-    }
-    if (t < n_tiles) {
-      tile_step(t, smem, smem + SB, false);
-      tile_end(false);
-    }
-  } else {
-    int buf = 0;  // t % NBUF
-    for (int t = 0; t < n_tiles; ++t) {
-      const bool prefetch = t + PD < n_tiles;
-      const int pb = (buf + PD >= NBUF) ? buf + PD - NBUF : buf + PD;
-      tile_step(t, smem + buf * SB, smem + pb * SB, prefetch);
-      tile_end(prefetch);
-      buf = (buf + 1 == NBUF) ? 0 : buf + 1;
-    }
+  // Two tiles per iteration, so that each one's buffers are constants and the LDS
+  // read addresses need no per-tile add.
+  TileRef cur = first;
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    TileRef nx = advance(cur);
+    tile_step(cur, nx, smem, smem + SB, true);
+    tile_end();
+    cur = nx;
+    nx = advance(cur);
+    tile_step(cur, nx, smem + SB, smem, t + 2 < n_tiles);
+    tile_end();
+    cur = nx;
+  }
+  if (t < n_tiles) {
+    tile_step(cur, cur, smem, smem + SB, false);
+    tile_end();
   }
 
   // ---- epilogue: normalise, write O (bf16) and LSE (natural log)
