@@ -288,7 +288,9 @@ void block_attention_kernel(const AttnArgs a) {
   asm volatile("" : "+s"(sl2));
 
   // ---- prologue
-  __syncthreads();  // LDS zeroed before the first DMA lands
+  // LDS zeroed in every wave before the first DMA lands.  No wait for the q loads
+  // here: they stay in flight beside the first tile's DMA.
+  barrier_lds_drained();
   if (n_tiles > 0)
     issue_tile_loads<KI, KIK, NKL, NW, BN>(first, kv_row_bytes, wave, smem + wave * 1024,
                                            smem + KTB + wave * KI * 1024, koff, voff);
@@ -300,14 +302,24 @@ void block_attention_kernel(const AttnArgs a) {
   // wait for the in-flight DMA before reading `cur`.
   auto tile_step = [&](const TileRef &cur, const TileRef &nx, const uint8_t *__restrict__ cur_buf,
                        uint8_t *__restrict__ nxt, bool prefetch) {
+    const uint8_t *Ks = cur_buf;
+    const uint8_t *Vs = cur_buf + KTB;
+    const bool wave_active = !(cur.seg == 2 && cur.k0 > rw + 32 * NSUB - 1);
+    // K fragments of block kb+1 are read into the slots that block kb has used,
+    // so KK reads are in flight ahead of the MFMAs.  The first reads go out
+    // before the next tile's DMA is set up, so their latency covers that work.
+    const uint8_t *kr = Ks + k_rd;
+    bf16x8 kf[KK];
+    if (wave_active) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kf[kk] = *reinterpret_cast<const bf16x8 *>(kr + kk * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (prefetch) {
       issue_tile_loads<KI, KIK, NKL, NW, BN>(nx, kv_row_bytes, wave, nxt + wave * 1024,
                                              nxt + KTB + wave * KI * 1024, koff, voff);
     }
-
-    const uint8_t *Ks = cur_buf;
-    const uint8_t *Vs = cur_buf + KTB;
-    const bool wave_active = !(cur.seg == 2 && cur.k0 > rw + 32 * NSUB - 1);
+    __builtin_amdgcn_sched_barrier(0);
     if (wave_active) {
       // S^T = K Q^T, one 32-key block at a time
       f32x16 sacc[NSUB][NKB];
@@ -315,12 +327,6 @@ void block_attention_kernel(const AttnArgs a) {
       for (int s = 0; s < NSUB; ++s)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) sacc[s][kb] = f32x16{};
-      // K fragments of block kb+1 are read into the slots that block kb has used,
-      // so KK reads are in flight ahead of the MFMAs.
-      const uint8_t *kr = Ks + k_rd;
-      bf16x8 kf[KK];
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kf[kk] = *reinterpret_cast<const bf16x8 *>(kr + kk * 32);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -333,7 +339,6 @@ void block_attention_kernel(const AttnArgs a) {
       }
 #if APB_ATTN_SCHED
       // K reads run KK MFMAs ahead of their use
-      __builtin_amdgcn_sched_group_barrier(0x100, KK, 0);
 #pragma unroll
       for (int i = 0; i < (NKB - 1) * KK * NSUB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -341,6 +346,20 @@ void block_attention_kernel(const AttnArgs a) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, KK * NSUB, 0);
 #endif
+
+      // V fragment (A operand of O^T += V^T P^T) for keys kb*32 + c*8 .. +7 and
+      // head-dim block db: 8 keys x 32 head-dim rows from two transposing reads.
+      auto v_frag = [&](int kb, int c, int db) {
+        const uint8_t *vb = Vs + (kb * 32 + c * 8) * ROWB + v_rd[db];
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(vb));
+        const v4i16 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(vb + 4 * ROWB));
+        return __builtin_bit_cast(bf16x8, (__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
+      };
+      // The first DB fragments are read before the softmax, which hides their latency.
+      bf16x8 vfr[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vfr[db] = v_frag(0, 0, db);
 
       const bool need_mask = (cur.k0 + BN > cur.seg_len) || (cur.seg == 2 && cur.k0 + BN - 1 > rw);
       bf16x8 pf[NSUB][NKB][2];
@@ -400,27 +419,23 @@ void block_attention_kernel(const AttnArgs a) {
         l_run[s] += psum;
       }
 
-      // O^T += V^T P^T; A operand = 8 keys x 32 head-dim rows from two transposing reads
+      // O^T += V^T P^T; the next (kb, c) fragment of head-dim block db is read into
+      // the slot its MFMA has just used
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const uint8_t *vb = Vs + (kb * 32 + c * 8) * ROWB + v_rd[db];
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(vb));
-            const v4i16 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(vb + 4 * ROWB));
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, (__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
 #pragma unroll
             for (int s = 0; s < NSUB; ++s)
-              acc[s][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s][kb][c], acc[s][db], 0, 0, 0);
+              acc[s][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[db], pf[s][kb][c], acc[s][db], 0, 0, 0);
+            if (kb * 2 + c + 1 < NKB * 2) vfr[db] = v_frag(c == 1 ? kb + 1 : kb, c ^ 1, db);
           }
         }
       }
 #if APB_ATTN_SCHED
-      // transposing V reads run four MFMAs ahead of their use
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+      // transposing V reads run DB MFMAs ahead of their use
 #pragma unroll
       for (int i = 0; i < NKB * 2 * DB - 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, NSUB, 1);
