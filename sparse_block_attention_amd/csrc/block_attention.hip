@@ -449,7 +449,7 @@ void block_attention_kernel(const AttnArgs a) {
   // Tile t+1 must have landed in every wave before the barrier that ends tile t.
   auto tile_end = [&]() {
     wait_vmcnt<0>();
-    barrier_keep_dma();
+    barrier_lds_drained();
   };
   // Two tiles per iteration, so that each one's buffers are constants and the LDS
   // read addresses need no per-tile add.
