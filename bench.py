@@ -388,8 +388,8 @@ def main():
                          "(a known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the per-host path has no collective in this build "
-              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only: it measures one host's block, and the exchange between "
+              f"hosts is not part of this library (--gpus {args.gpus} requested)", file=sys.stderr)
         sys.exit(2)
 
     import torch

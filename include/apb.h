@@ -58,7 +58,7 @@ extern "C" {
 typedef enum {
   APB_OK = 0,
   APB_ERR_INVALID_ARGUMENT = 1, /* NULL / misaligned pointer, inconsistent sizes */
-  APB_ERR_UNSUPPORTED = 2,      /* valid in principle, outside this build's limits */
+  APB_ERR_UNSUPPORTED = 2,      /* valid in principle, outside this library's limits */
   APB_ERR_HIP = 3,              /* the HIP runtime reported an error */
   APB_ERR_INTERNAL = 4
 } apb_status;

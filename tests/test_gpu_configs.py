@@ -7,7 +7,7 @@ oracle fed the GPU's previous-stage output:
   * top-l indices of every kv head over the whole block, bit-exact;
   * the compressed block (gather), bit-exact;
   * the passing block built from seeded compressed blocks of the 7 earlier
-    hosts, bit-exact (those blocks are inputs of the build step; drawing them
+    hosts, bit-exact (those blocks are inputs of the passing assembly; drawing them
     directly saves compressing 7 more full-size host blocks);
   * attention on sampled rows of every q head.
 """
