@@ -35,8 +35,15 @@
 //    sum, and recomputes.  The final normalisation makes this exact; every p
 //    stays far below the fp32 and bf16 range.  The row max is exchanged between
 //    lane halves with v_permlane32_swap; row sums stay per lane until the end.
+//  * The tile loop runs two tiles per iteration, so both buffers' LDS addresses
+//    are loop-invariant registers plus immediates, and walks the tiles with a
+//    cursor (pointer bumps; a branch only where a segment ends).  Each tile
+//    issues its K reads before it sets up the next tile's DMA, and reads its
+//    first V fragments before the softmax.
 #include "apb_internal.h"
 
+// Workgroup shape and tile size of the head_dim 128 instance (the defaults are
+// the measured best; the head_dim 64 instance is fixed at 1, 64, 4, 2).
 #ifndef APB_ATTN_NSUB
 #define APB_ATTN_NSUB 1
 #endif
@@ -437,11 +444,11 @@ void block_attention_kernel(const AttnArgs a) {
 #if APB_ATTN_SCHED
       // transposing V reads run DB MFMAs ahead of their use
 #pragma unroll
-      for (int i = 0; i < NKB * 2 * DB - 4; ++i) {
+      for (int i = 0; i < NKB * 2 * DB - DB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, NSUB, 1);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * NSUB, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, DB * NSUB, 1);
 #endif
     }
   };
