@@ -1,0 +1,72 @@
+"""Host-side checks of bench.py's accounting (no GPU).
+
+* attention_flops: 4 d Hq times the visible (row, key) pairs.  The pair count is
+  taken from the oracle itself: with q = 0 every visible key gets the same
+  weight, so exp(lse) of a row is its number of visible keys.
+* attention_bytes: q, the anchor/passing/local K and V, O and LSE, each once, as
+  the arrays a launch reads and writes.
+* the traffic record is only used for its own workload, and bench refuses more
+  than one GPU before touching a device.
+"""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import apb_oracle as orc
+from sparse_block_attention_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _small(L, A, l, host, Hq, Hkv, d):
+    return synth.Workload("acct", 900, host + 1, L, A, l, Hq, Hkv, d, 32, 1.0, 0)
+
+
+@pytest.mark.parametrize("L,A,l,host,Hq,Hkv,d", [
+    (37, 5, 3, 2, 2, 1, 64), (64, 0, 4, 1, 4, 2, 128), (20, 9, 0, 3, 3, 3, 64), (1, 1, 1, 1, 2, 2, 128),
+])
+def test_attention_flops_count_the_oracles_visible_pairs(bench, L, A, l, host, Hq, Hkv, d):
+    w = _small(L, A, l, host, Hq, Hkv, d)
+    P = w.pass_len
+    rng = np.random.default_rng(L + A)
+    q = np.zeros((L, Hq, d))
+    kv = lambda n: (rng.standard_normal((n, Hkv, d)), rng.standard_normal((n, Hkv, d)))
+    (ka, va), (kp, vp), (kl, vl) = kv(A), kv(P), kv(L)
+    _, lse = orc.block_attention(q, ka, va, kp, vp, kl, vl)
+    pairs_per_head = np.exp(lse).sum(axis=1)            # visible keys summed over rows, per q head
+    assert np.allclose(pairs_per_head, pairs_per_head[0])
+    assert bench.attention_flops(w) == pytest.approx(4.0 * d * Hq * pairs_per_head[0], rel=1e-12)
+
+
+def test_attention_bytes_are_the_arrays_of_one_launch(bench):
+    w = synth.WORKLOADS["llama8b"]
+    L, A, P, Hq, Hkv, d = w.local_len, w.anchor_len, w.pass_len, w.n_q_heads, w.n_kv_heads, w.head_dim
+    bf16, f32 = 2, 4
+    reads = L * Hq * d * bf16 + 2 * (A + P + L) * Hkv * d * bf16   # q, K and V of three segments
+    writes = L * Hq * d * bf16 + Hq * L * f32                       # O and LSE
+    assert bench.attention_bytes(w) == reads + writes
+    assert bench.attention_flops(w) == pytest.approx(4.673058635776e12, rel=1e-12)
+
+
+def test_traffic_record_is_used_only_for_its_workload(bench):
+    assert bench.measured_traffic("qwen14b") is None
+    assert bench.measured_traffic("tiny") is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU only" in r.stderr
