@@ -78,6 +78,22 @@ def attention_bytes(w) -> float:
     return 2.0 * L * Hq * d * 2 + 2.0 * (A + P + L) * Hkv * d * 2 + 4.0 * Hq * L
 
 
+def stage_bytes(w) -> dict:
+    """Algorithmic HBM bytes of the compression steps and the passing build of one host."""
+    L, Hq, Hkv, d, l, hs = (w.local_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.pass_per_host,
+                            w.hidden)
+    g = Hq // Hkv
+    return {
+        # q, k, v of the block, W1, b1, w2 and b2 read; fp32 scores written
+        "a1_score": L * (Hq + 2 * Hkv) * d * 2 + Hkv * hs * (g + 2) * d * 2 + Hkv * (2 * hs + 1) * 4
+        + Hkv * L * 4,
+        # scores read; l rows of K and V per kv head read and written; indices written
+        "a2a3_topl_gather": Hkv * L * 4 + 2 * 2 * l * Hkv * d * 2 + Hkv * l * 4,
+        # the earlier hosts' compressed blocks of K and V read and written once
+        "a5_passing": 2 * 2 * w.pass_len * Hkv * d * 2,
+    }
+
+
 def _src_hash(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -143,9 +159,6 @@ def stages(B, w, pr, sc, host, ka, va, kcs, vcs, buf, reps=20, warm=5):
     which evicts the 256 MB Infinity Cache and leaves it clean.  Cold dirty: the 512 MB
     buffer is written instead; the step then also pays for writing back the dirty lines."""
     import torch
-    L, Hq, Hkv, d, l, hs = (w.local_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.pass_per_host,
-                            w.hidden)
-    g = Hq // Hkv
     scratch = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
     scratch_i = scratch.view(torch.int32)
     total = torch.zeros((), dtype=torch.int64, device="cuda")
@@ -161,15 +174,7 @@ def stages(B, w, pr, sc, host, ka, va, kcs, vcs, buf, reps=20, warm=5):
         fill[0] = (fill[0] + 1) & 0xFF
         scratch.fill_(fill[0])
 
-    byt = {
-        # q, k, v of the block, W1, b1, w2 and b2 read; fp32 scores written
-        "a1_score": L * (Hq + 2 * Hkv) * d * 2 + Hkv * hs * (g + 2) * d * 2 + Hkv * (2 * hs + 1) * 4
-        + Hkv * L * 4,
-        # scores read; l rows of K and V per kv head read and written; indices written
-        "a2a3_topl_gather": Hkv * L * 4 + 2 * 2 * l * Hkv * d * 2 + Hkv * l * 4,
-        # p compressed blocks of K and V read and written once
-        "a5_passing": 2 * 2 * pr.pass_len * Hkv * d * 2,
-    }
+    byt = stage_bytes(w)
     fns = {
         "a1_score": lambda: B.apb_score_kv(pr, sc, host.q, host.k, host.v, scores=buf.scores),
         "a2a3_topl_gather": lambda: B.apb_topk_gather(pr, buf.scores, host.k, host.v, idx=buf.idx,

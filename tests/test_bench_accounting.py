@@ -4,7 +4,8 @@
   taken from the oracle itself: with q = 0 every visible key gets the same
   weight, so exp(lse) of a row is its number of visible keys.
 * attention_bytes: q, the anchor/passing/local K and V, O and LSE, each once, as
-  the arrays a launch reads and writes.
+  the arrays a launch reads and writes; stage_bytes likewise for the scorer,
+  top-l + gather and the passing build.
 * the traffic record is only used for its own workload, and bench refuses more
   than one GPU before touching a device.
 """
@@ -70,3 +71,21 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode != 0
     assert "one GPU only" in r.stderr
+
+
+def test_stage_bytes_are_the_arrays_each_step_moves(bench):
+    """Scorer: q, k, v of the block, the scorer weights and the fp32 scores; top-l +
+    gather: scores, K and V rows read and written, indices; passing: the earlier
+    hosts' compressed blocks read and written.  Sizes from the generator's arrays."""
+    w = synth.Workload("acct_stage", 901, 3, 40, 8, 6, 4, 2, 64, 32, 1.0, 0)
+    q, k, v = synth.host_block(w, w.host)
+    wts = synth.scorer_weights(w)
+    scores = np.zeros((w.n_kv_heads, w.local_len), np.float32)
+    idx = np.zeros((w.n_kv_heads, w.pass_per_host), np.int32)
+    bf16 = lambda a: a.size * 2
+    kv_row = w.n_kv_heads * w.head_dim * 2
+    b = bench.stage_bytes(w)
+    assert b["a1_score"] == (bf16(q) + bf16(k) + bf16(v) + bf16(wts["w1"]) + wts["b1"].size * 4
+                             + wts["w2"].size * 4 + wts["b2"].size * 4 + scores.nbytes)
+    assert b["a2a3_topl_gather"] == scores.nbytes + 2 * 2 * w.pass_per_host * kv_row + idx.nbytes
+    assert b["a5_passing"] == 2 * 2 * w.host * w.pass_per_host * kv_row
