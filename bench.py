@@ -333,6 +333,33 @@ def layer_sides(B, w, host, ka, va, reps=10, warm=3):
     return res
 
 
+def _tiny_step_single_thread():
+    """Seconds for the whole tiny host step (scoring, top-l, gather, passing build and
+    attention of every row) in the CPU oracle on one BLAS thread, or None without
+    threadpoolctl."""
+    from oracle import apb_oracle as orc
+    from sparse_block_attention_amd import synth
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover - threadpoolctl is optional
+        return None
+    wt = synth.WORKLOADS["tiny"]
+    q, k, v = synth.host_block(wt, wt.host)
+    wts = synth.scorer_weights(wt)
+    ka, va = synth.anchor_kv(wt)
+    comps = [(synth.random_bf16((wt.pass_per_host, wt.n_kv_heads, wt.head_dim), 92, stream=j),
+              synth.random_bf16((wt.pass_per_host, wt.n_kv_heads, wt.head_dim), 93, stream=j))
+             for j in range(wt.host)]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        s = orc.score_kv(q, k, v, wts["w1"], wts["b1"], wts["w2"], wts["b2"])
+        orc.gather(k, v, orc.topl(s, wt.pass_per_host))
+        kp, vp = orc.build_passing([c[0] for c in comps], [c[1] for c in comps])
+        orc.block_attention(q, ka, va, kp, vp, k, v)
+        t1 = time.perf_counter()
+    return round(t1 - t0, 4)
+
+
 def cpu_baseline(w, blocks, weights, anchor, n_rows=4096):
     """Time the CPU oracle on a bounded sample of one host step; scale to tokens/s."""
     from oracle import apb_oracle as orc
@@ -367,6 +394,7 @@ def cpu_baseline(w, blocks, weights, anchor, n_rows=4096):
     t_total = (t1 - t0) + (t2 - t1) + (t3 - t2b) + t_attn
     return {
         "value": L / t_total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+        "tiny_step_single_thread_s": _tiny_step_single_thread(),
         "sample": (f"scoring, top-l and gather over the whole {L}-token block; passing build of "
                    f"{w.host} blocks; attention for {n_rows} evenly spaced query rows x "
                    f"{w.n_q_heads} heads ({sample_pairs} of {all_pairs} visible pairs per head, "
