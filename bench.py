@@ -178,7 +178,8 @@ def stages(B, w, pr, sc, host, ka, va, kcs, vcs, buf, reps=20, warm=5):
     fns = {
         "a1_score": lambda: B.apb_score_kv(pr, sc, host.q, host.k, host.v, scores=buf.scores),
         "a2a3_topl_gather": lambda: B.apb_topk_gather(pr, buf.scores, host.k, host.v, idx=buf.idx,
-                                                      k_comp=buf.k_comp, v_comp=buf.v_comp),
+                                                      k_comp=buf.k_comp, v_comp=buf.v_comp,
+                                                      workspace=buf.topk_workspace),
     }
     if pr.pass_len:
         fns["a5_passing"] = lambda: B.apb_build_passing(pr, kcs, vcs, k_pass=buf.k_pass, v_pass=buf.v_pass)

@@ -48,19 +48,21 @@
 extern "C" {
 #endif
 
-#define APB_ABI_VERSION 4
+#define APB_ABI_VERSION 5
 
 /* Upper limits of this implementation (APB_ERR_UNSUPPORTED beyond them). */
 #define APB_MAX_Q_HEADS 256
 #define APB_MAX_LOCAL_LEN (1 << 26)
 #define APB_MAX_PASS_HOSTS_PER_LAUNCH 128
+#define APB_MAX_ROPE_POSITION (1LL << 31) /* apb_rope: pos0 + rows <= this */
 
 typedef enum {
   APB_OK = 0,
-  APB_ERR_INVALID_ARGUMENT = 1, /* NULL / misaligned pointer, inconsistent sizes */
-  APB_ERR_UNSUPPORTED = 2,      /* valid in principle, outside this library's limits */
-  APB_ERR_HIP = 3,              /* the HIP runtime reported an error */
-  APB_ERR_INTERNAL = 4
+  APB_ERR_INVALID_ARGUMENT = 1,    /* NULL / misaligned pointer, inconsistent sizes */
+  APB_ERR_UNSUPPORTED = 2,         /* valid in principle, outside this library's limits */
+  APB_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below apb_topk_workspace_size() */
+  APB_ERR_HIP = 4,                 /* the HIP runtime reported an error */
+  APB_ERR_INTERNAL = 5             /* unexpected failure inside the library */
 } apb_status;
 
 /*
@@ -94,7 +96,7 @@ typedef struct {
  * Device pointers.  Products of bf16 values are accumulated in fp32.
  */
 typedef struct {
-  int32_t hidden;          /* Hs: a multiple of 32, 32..256                    */
+  int32_t hidden;          /* Hs: a multiple of 16, 16..256                    */
   const void *w1;          /* bf16 [Hkv][Hs][(g+2)*d]  (nn.Linear weight layout) */
   const float *b1;         /* fp32 [Hkv][Hs]                                    */
   const float *w2;         /* fp32 [Hkv][Hs]                                    */
@@ -120,11 +122,25 @@ apb_status apb_score_kv(const apb_problem *problem, const apb_scorer *scorer,
  *   k_local, v_local bf16 [L][Hkv][d]
  *   idx             int32 [Hkv][l] (output) selected local token indices, ascending
  *   k_comp, v_comp  bf16 [l][Hkv][d] (output) k_comp[s][h] = k_local[idx[h][s]][h]
- * With l == 0 nothing is written and the pointers may be NULL.
+ *   workspace       device scratch of at least apb_topk_workspace_size(problem)
+ *                   bytes, 16-byte aligned, owned by the caller.  Its contents on
+ *                   entry do not matter (every byte the call reads, it wrote
+ *                   earlier in the same call) and are meaningless afterwards; two
+ *                   calls in flight at once need two workspaces.
+ * With l == 0 nothing is written and every pointer may be NULL.  A workspace
+ * smaller than required returns APB_ERR_WORKSPACE_TOO_SMALL and launches nothing.
  */
+/*
+ * Bytes of workspace apb_topk_gather needs for `problem` (a few bytes per kv
+ * head plus 8 bytes per 256 local tokens per kv head).  Returns 0 when the
+ * problem is invalid (apb_last_error() says why) or when l == 0, where the
+ * call does nothing and needs no workspace.  Host-only; launches nothing.
+ */
+size_t apb_topk_workspace_size(const apb_problem *problem);
 apb_status apb_topk_gather(const apb_problem *problem, const float *scores,
                            const void *k_local, const void *v_local,
-                           int32_t *idx, void *k_comp, void *v_comp, void *stream);
+                           int32_t *idx, void *k_comp, void *v_comp,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Step 3: passing block from the compressed blocks of hosts 0..p-1 (explainer,
@@ -231,10 +247,12 @@ apb_status apb_anchor_attention(const apb_problem *problem, const void *q_anchor
  *     out[r][h][i]       = x[r][h][i] cos(a) - x[r][h][i + d/2] sin(a)
  *     out[r][h][i + d/2] = x[r][h][i] sin(a) + x[r][h][i + d/2] cos(a)
  *   x, out   bf16 [rows][heads][d], d in {64, 128}; out may be x (in place)
- * theta_i is computed on the host in double precision, a is reduced modulo 2*pi
- * in double precision on the device, the rotation is done in fp32 and rounded
- * once to bf16 (nearest even).  rows >= 1, 1 <= heads <= 4096, pos0 >= 0,
- * theta_base > 1 and finite.
+ * theta_i is computed on the host in double precision, a is formed and reduced
+ * modulo 2*pi in double precision on the device, the rotation is done in fp32
+ * and rounded once to bf16 (nearest even).  Positions are capped so that the
+ * double-precision angle stays within 2^31 * 2^-52 = 2^-21 rad of the exact one,
+ * far below the bf16 rounding of the output.  rows >= 1, 1 <= heads <= 4096,
+ * pos0 >= 0, pos0 + rows <= APB_MAX_ROPE_POSITION, theta_base > 1 and finite.
  */
 apb_status apb_rope(const void *x, void *out, int32_t rows, int32_t heads, int32_t head_dim, int64_t pos0,
                     float theta_base, void *stream);

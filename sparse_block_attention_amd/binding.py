@@ -22,8 +22,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libapb.so")
 APB_OK = 0
 APB_ERR_INVALID_ARGUMENT = 1
 APB_ERR_UNSUPPORTED = 2
-APB_ERR_HIP = 3
-APB_ERR_INTERNAL = 4
+APB_ERR_WORKSPACE_TOO_SMALL = 3
+APB_ERR_HIP = 4
+APB_ERR_INTERNAL = 5
 
 APB_SEG_ANCHOR = 1
 APB_SEG_PASSING = 2
@@ -67,10 +68,14 @@ class Problem:
         return self.host_index * self.pass_per_host
 
     def to_c(self):
-        """(ctypes struct, keep-alive array) for a call."""
+        """(ctypes struct, keep-alive array) for a call.  The library reads n_q_heads
+        entries of the head map, so a map of any other length is refused here."""
         arr = None
         ptr = None
         if self.kv_head_of_q is not None:
+            if len(self.kv_head_of_q) != self.n_q_heads:
+                raise ValueError(f"kv_head_of_q has {len(self.kv_head_of_q)} entries, "
+                                 f"need n_q_heads = {self.n_q_heads}")
             arr = (c_int32 * len(self.kv_head_of_q))(*[int(x) for x in self.kv_head_of_q])
             ptr = ctypes.cast(arr, POINTER(c_int32))
         s = _Problem(self.n_q_heads, self.n_kv_heads, self.head_dim, self.local_len,
@@ -92,7 +97,9 @@ def lib() -> ctypes.CDLL:
         P = POINTER(_Problem)
         L.apb_score_kv.argtypes = [P, POINTER(_Scorer), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
         L.apb_topk_gather.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                      c_void_p]
+                                      c_void_p, ctypes.c_size_t, c_void_p]
+        L.apb_topk_workspace_size.argtypes = [P]
+        L.apb_topk_workspace_size.restype = ctypes.c_size_t
         L.apb_build_passing.argtypes = [P, POINTER(c_void_p), POINTER(c_void_p), c_void_p, c_void_p,
                                         c_void_p]
         L.apb_block_attention.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -175,9 +182,25 @@ def apb_score_kv(problem: Problem, scorer: dict, q_local, k_local, v_local, scor
     return scores
 
 
+def apb_topk_workspace_size(problem: Problem) -> int:
+    """Bytes of workspace apb_topk_gather needs (0 for l == 0 or an invalid problem)."""
+    cp, keep = problem.to_c()
+    n = lib().apb_topk_workspace_size(ctypes.byref(cp))
+    del keep
+    return int(n)
+
+
+def topk_workspace(problem: Problem, device="cuda") -> torch.Tensor:
+    """A uint8 device tensor of apb_topk_workspace_size(problem) bytes (at least 1)."""
+    return torch.empty(max(apb_topk_workspace_size(problem), 1), dtype=torch.uint8, device=device)
+
+
 def apb_topk_gather(problem: Problem, scores, k_local, v_local, idx=None, k_comp=None, v_comp=None,
-                    stream=None):
-    """(idx int32 [Hkv, l], k_comp, v_comp bf16 [l, Hkv, d]) (see include/apb.h)."""
+                    workspace=None, stream=None):
+    """(idx int32 [Hkv, l], k_comp, v_comp bf16 [l, Hkv, d]) (see include/apb.h).
+
+    `workspace` is a uint8 device tensor of at least apb_topk_workspace_size(problem)
+    bytes; None allocates one for this call."""
     pr = problem
     L, Hkv, d, l = pr.local_len, pr.n_kv_heads, pr.head_dim, pr.pass_per_host
     dev = scores.device
@@ -187,13 +210,19 @@ def apb_topk_gather(problem: Problem, scores, k_local, v_local, idx=None, k_comp
         k_comp = torch.empty((l, Hkv, d), dtype=torch.bfloat16, device=dev)
     if v_comp is None:
         v_comp = torch.empty((l, Hkv, d), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = topk_workspace(pr, dev)
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
+            or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the GPU")
     cp, keep = pr.to_c()
     st = lib().apb_topk_gather(ctypes.byref(cp), _ptr(scores, "scores", torch.float32, (Hkv, L)),
                                _ptr(k_local, "k_local", torch.bfloat16, (L, Hkv, d)),
                                _ptr(v_local, "v_local", torch.bfloat16, (L, Hkv, d)),
                                _ptr(idx, "idx", torch.int32, (Hkv, l)),
                                _ptr(k_comp, "k_comp", torch.bfloat16, (l, Hkv, d)),
-                               _ptr(v_comp, "v_comp", torch.bfloat16, (l, Hkv, d)), _stream(stream))
+                               _ptr(v_comp, "v_comp", torch.bfloat16, (l, Hkv, d)),
+                               workspace.data_ptr(), workspace.numel(), _stream(stream))
     del keep
     _check(st, "apb_topk_gather")
     return idx, k_comp, v_comp

@@ -101,15 +101,21 @@ struct ScoreArgs {
 };
 hipError_t launch_score_kv(ScoreArgs &a, hipStream_t s);
 
-// Top-l selection + gather.
+// Top-l selection + gather.  The workspace holds, per kv head, the selection
+// state {T, need} and, per chunk of 256 keys, the counts of keys > T and == T in
+// the chunks before it.
 struct TopkArgs {
   const float *scores;
   const uint16_t *k, *v;
   int32_t *idx;
   uint16_t *kc, *vc;
+  uint32_t *state;          // [Hkv][2]            (workspace)
+  uint32_t *chunk_counts;   // [Hkv][n_chunks][2]  (workspace)
   int L, l, Hkv, d;
+  int n_chunks;             // ceil(L / 256)
 };
-hipError_t launch_topk_gather(const TopkArgs &a, hipStream_t s);
+size_t topk_workspace_bytes(int L, int Hkv);
+hipError_t launch_topk_gather(TopkArgs &a, void *workspace, hipStream_t s);
 
 // Passing-block assembly: up to 128 source blocks per launch.
 struct PassArgs {

@@ -32,8 +32,8 @@ apb_status score_kv(const apb_problem *pr, const apb_scorer *sc, const void *q, 
                     float *scores, void *stream) {
   APB_TRY(apb_host::check_problem(pr));
   if (sc == nullptr) return fail(APB_ERR_INVALID_ARGUMENT, "scorer is NULL");
-  if (sc->hidden < 32 || sc->hidden > 256 || sc->hidden % 32 != 0)
-    return fail(APB_ERR_UNSUPPORTED, "scorer hidden = %d, supported: multiples of 32 in [32, 256]", sc->hidden);
+  if (sc->hidden < 16 || sc->hidden > 256 || sc->hidden % 16 != 0)
+    return fail(APB_ERR_UNSUPPORTED, "scorer hidden = %d, supported: multiples of 16 in [16, 256]", sc->hidden);
   APB_TRY(need_ptr(sc->w1, "scorer.w1"));
   APB_TRY(need_ptr(sc->b1, "scorer.b1"));
   APB_TRY(need_ptr(sc->w2, "scorer.w2"));
@@ -63,7 +63,7 @@ apb_status score_kv(const apb_problem *pr, const apb_scorer *sc, const void *q, 
 }
 
 apb_status topk_gather(const apb_problem *pr, const float *scores, const void *k, const void *v, int32_t *idx,
-                       void *kc, void *vc, void *stream) {
+                       void *kc, void *vc, void *ws, size_t ws_bytes, void *stream) {
   APB_TRY(apb_host::check_problem(pr));
   if (pr->pass_per_host == 0) return APB_OK;
   APB_TRY(need_ptr(scores, "scores"));
@@ -72,7 +72,13 @@ apb_status topk_gather(const apb_problem *pr, const float *scores, const void *k
   APB_TRY(need_ptr(idx, "idx"));
   APB_TRY(need_ptr(kc, "k_comp"));
   APB_TRY(need_ptr(vc, "v_comp"));
+  const size_t need_bytes = apb::topk_workspace_bytes(pr->local_len, pr->n_kv_heads);
+  if (ws_bytes < need_bytes)
+    return fail(APB_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes = %zu, need %zu (apb_topk_workspace_size)", ws_bytes,
+                need_bytes);
+  APB_TRY(need_ptr(ws, "workspace"));
   apb::TopkArgs a;
+  memset(&a, 0, sizeof a);
   a.scores = scores;
   a.k = static_cast<const uint16_t *>(k);
   a.v = static_cast<const uint16_t *>(v);
@@ -83,7 +89,13 @@ apb_status topk_gather(const apb_problem *pr, const float *scores, const void *k
   a.l = pr->pass_per_host;
   a.Hkv = pr->n_kv_heads;
   a.d = pr->head_dim;
-  return hip_status(apb::launch_topk_gather(a, static_cast<hipStream_t>(stream)), "apb_topk_gather launch");
+  return hip_status(apb::launch_topk_gather(a, ws, static_cast<hipStream_t>(stream)), "apb_topk_gather launch");
+}
+
+size_t topk_workspace_size(const apb_problem *pr) {
+  if (apb_host::check_problem(pr) != APB_OK) return 0;
+  if (pr->pass_per_host == 0) return 0;
+  return apb::topk_workspace_bytes(pr->local_len, pr->n_kv_heads);
 }
 
 apb_status build_passing(const apb_problem *pr, const void *const *kh, const void *const *vh, void *kp, void *vp,
@@ -193,8 +205,9 @@ apb_status rope(const void *x, void *out, int32_t rows, int32_t heads, int32_t d
   if (rows < 1) return fail(APB_ERR_INVALID_ARGUMENT, "rows = %d, need >= 1", rows);
   if (heads < 1 || heads > 4096) return fail(APB_ERR_INVALID_ARGUMENT, "heads = %d, need 1..4096", heads);
   if (d != 64 && d != 128) return fail(APB_ERR_UNSUPPORTED, "head_dim = %d, supported: 64, 128", d);
-  if (pos0 < 0 || pos0 + rows > (1LL << 53))
-    return fail(APB_ERR_INVALID_ARGUMENT, "pos0 = %lld: positions must lie in [0, 2^53)", (long long)pos0);
+  if (pos0 < 0 || pos0 + rows > APB_MAX_ROPE_POSITION)
+    return fail(APB_ERR_INVALID_ARGUMENT, "pos0 = %lld, rows = %d: positions must lie in [0, 2^31)",
+                (long long)pos0, rows);
   if (!(base > 1.f) || !isfinite(base))
     return fail(APB_ERR_INVALID_ARGUMENT, "theta_base = %g, need finite and > 1", (double)base);
   apb::RopeArgs a;
@@ -280,9 +293,21 @@ apb_status apb_score_kv(const apb_problem *problem, const apb_scorer *scorer, co
   APB_GUARD(score_kv(problem, scorer, q_local, k_local, v_local, scores, stream));
 }
 
+size_t apb_topk_workspace_size(const apb_problem *problem) {
+  try {
+    apb_host::clear_error();
+    return topk_workspace_size(problem);
+  } catch (...) {
+    fail(APB_ERR_INTERNAL, "unexpected C++ exception in %s", __func__);
+    return 0;
+  }
+}
+
 apb_status apb_topk_gather(const apb_problem *problem, const float *scores, const void *k_local,
-                           const void *v_local, int32_t *idx, void *k_comp, void *v_comp, void *stream) {
-  APB_GUARD(topk_gather(problem, scores, k_local, v_local, idx, k_comp, v_comp, stream));
+                           const void *v_local, int32_t *idx, void *k_comp, void *v_comp, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  APB_GUARD(topk_gather(problem, scores, k_local, v_local, idx, k_comp, v_comp, workspace, workspace_bytes,
+                        stream));
 }
 
 apb_status apb_build_passing(const apb_problem *problem, const void *const *k_comp_hosts,

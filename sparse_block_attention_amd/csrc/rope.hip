@@ -10,8 +10,9 @@
 // from each half of a head row) and keeps their (cos, sin) for every head of
 // the row, since the angle depends on the position and i only.  The angle
 // pos * theta_i is formed and reduced modulo 2*pi in double precision
-// (Cody-Waite with a two-part 2*pi), so positions up to 2^26 lose nothing;
-// sin/cos and the rotation run in fp32 and each output is rounded once to bf16.
+// (Cody-Waite with a two-part 2*pi): with positions below 2^31 the reduced angle
+// is within about 2^-21 rad of the exact one; sin/cos and the rotation run in
+// fp32 and each output is rounded once to bf16.
 #include "apb_internal.h"
 
 namespace apb {

@@ -149,7 +149,7 @@ __device__ __forceinline__ void score_chunk(f32x16 (&acc)[(HB + 3) / 4][4], cons
   }
 }
 
-template <int HB, int TH>  // hidden = 32 * HB; 128 * TH tokens per workgroup
+template <int HB, int TH>  // hidden in (32 * HB - 32, 32 * HB]; 128 * TH tokens per workgroup
 __global__ __launch_bounds__(ScoreCfg<TH>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void score_kv_kernel(const ScoreArgs a) {
   using C = ScoreCfg<TH>;
@@ -201,12 +201,15 @@ void score_kv_kernel(const ScoreArgs a) {
   const int valid_rows = min(L - t0, kTok);
   const int q_row_bytes = Hq * d * 2;
   const int kv_row_bytes = Hkv * d * 2;
-  const uint16_t *w1h = a.w1 + (size_t)h * HS * din;
-  const int w_valid = HS * din * 2;
+  // hidden = a.hidden <= HS: W1 rows past it read as zeros (the descriptor ends at
+  // the last row), and their b1 and w2 are zero, so padded units add nothing.
+  const int hidden = a.hidden;
+  const uint16_t *w1h = a.w1 + (size_t)h * hidden * din;
+  const int w_valid = hidden * din * 2;
 
   for (int i = tid; i < HS; i += kThreads) {
-    sb1[i] = b1[(size_t)h * HS + i];
-    sw2[i] = w2[(size_t)h * HS + i];
+    sb1[i] = i < hidden ? b1[(size_t)h * hidden + i] : 0.f;
+    sw2[i] = i < hidden ? w2[(size_t)h * hidden + i] : 0.f;
   }
   // Element offset of each x segment inside its tensor row: q heads of the group
   // (ascending), then k and v of head h.  The q-head table is read in place from
@@ -311,7 +314,7 @@ hipError_t launch_hs(ScoreArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_score_kv(ScoreArgs &a, hipStream_t s) {
-  switch (a.hidden / 32) {
+  switch ((a.hidden + 31) / 32) {
     case 1: return launch_hs<1>(a, s);
     case 2: return launch_hs<2>(a, s);
     case 3: return launch_hs<3>(a, s);

@@ -17,19 +17,23 @@
 //     chosen bin holds exactly the keys still needed, all of them are kept and
 //     the lower digits are skipped: T is the bin's lowest key and every key
 //     >= T is kept.
-//  2. a stable compaction in index order keeps every key > T and the first
-//     `need` keys == T.  With keys in LDS each thread owns a run of consecutive
-//     indices and one block scan of its counts places its kept keys; above
-//     that, each wave owns a contiguous run and ballots plus lane-mask bit
-//     counts place them.  Either way the result does not depend on timing.
-// gfx950 design: one 1024-thread workgroup (16 wave64s) per kv head.  Keys stay
-// in LDS (128 KB) when the block has at most 32768 tokens; otherwise every pass
-// re-reads the fp32 scores, which stay in L2 (512 KB per head at 131072
-// tokens).  Scans are wave scans (cross-lane shuffles) plus one barrier for the
-// 16 wave totals; starting the digits below the shared leading bits keeps the
-// LDS histogram atomics from piling onto a few bins.
-// The gather is a separate wide kernel: one workgroup per selected slot and
-// tensor, 16 bytes per thread, contiguous rows.
+//  2. per-chunk counts: for every chunk of 256 keys, the number of keys > T and
+//     == T in the chunks before it (an exclusive scan over the chunks).
+//  3. compaction and gather: a wide kernel, one workgroup per chunk, keeps every
+//     key > T and the first `need` keys == T in index order.  A kept key's slot
+//     is the number of kept keys before it, from its chunk's counts and wave
+//     ballots inside the chunk, so the result does not depend on timing; the
+//     same workgroup then copies the kept keys' K and V head rows.
+// gfx950 design: the select runs one 1024-thread workgroup (16 wave64s) per kv
+// head.  Keys stay in LDS (128 KB) when the block has at most 32768 tokens;
+// otherwise every pass re-reads the fp32 scores, which stay in L2 (512 KB per
+// head at 131072 tokens).  Scans are wave scans (cross-lane shuffles) plus one
+// barrier for the 16 wave totals; starting the digits below the shared leading
+// bits keeps the LDS histogram atomics from piling onto a few bins.  The select
+// hands T, `need` and the chunk counts to the placement kernel through the
+// caller's workspace; every workspace word a call reads was written earlier in
+// that call.  The placement kernel spreads the compaction and the 16-byte row
+// copies over L/256 x Hkv workgroups.
 #include "apb_internal.h"
 
 namespace apb {
@@ -65,6 +69,51 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
 // before it uses any, so a thread waits for one memory latency per batch rather
 // than one per key.
 constexpr int kBatch = 8;
+
+// Placement chunk (keys per workgroup of the placement kernel) and the run of
+// consecutive keys one thread of the select kernel counts per step.
+constexpr int kChunk = 256;
+constexpr int kRun = 16;
+
+// Keys r*kRun .. r*kRun+kRun-1 of one head (entries past L are unspecified): from
+// LDS when the keys are there, else from the fp32 scores, with 16-byte loads when
+// the row allows them.
+template <bool KEYS_IN_LDS>
+__device__ __forceinline__ void load_run(const TopkArgs &a, const float *srow, const uint32_t *keys, int r,
+                                         uint32_t (&kr)[kRun]) {
+  const int b = r * kRun;
+  if constexpr (KEYS_IN_LDS) {
+#pragma unroll
+    for (int j = 0; j < kRun; j += 4) {
+      const uint4 q4 = *reinterpret_cast<const uint4 *>(&keys[b + j]);
+      kr[j] = q4.x;
+      kr[j + 1] = q4.y;
+      kr[j + 2] = q4.z;
+      kr[j + 3] = q4.w;
+    }
+  } else {
+    if ((a.L & 3) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0) {
+      const int n4 = a.L >> 2;
+      const float4 *s4 = reinterpret_cast<const float4 *>(srow);
+      float4 f[kRun / 4];
+#pragma unroll
+      for (int j = 0; j < kRun / 4; ++j) f[j] = s4[min(b / 4 + j, n4 - 1)];
+#pragma unroll
+      for (int j = 0; j < kRun / 4; ++j) {
+        kr[4 * j] = order_key(f[j].x);
+        kr[4 * j + 1] = order_key(f[j].y);
+        kr[4 * j + 2] = order_key(f[j].z);
+        kr[4 * j + 3] = order_key(f[j].w);
+      }
+    } else {
+      float f[kRun];
+#pragma unroll
+      for (int j = 0; j < kRun; ++j) f[j] = srow[min(b + j, a.L - 1)];
+#pragma unroll
+      for (int j = 0; j < kRun; ++j) kr[j] = order_key(f[j]);
+    }
+  }
+}
 
 template <bool KEYS_IN_LDS>
 __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const TopkArgs a) {
@@ -218,138 +267,163 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const TopkArg
   const uint32_t T = prefix;
   // elements == T to keep, >= 1 (all of them after an early exit: keys > T and == T
   // are then both kept, at positions counting both)
+  // (common == 32: every key equals kmin, which is T)
   const uint32_t need = take_all_eq ? 0xffffffffu : (uint32_t)k_rem;
 
-  // (common == 32: every key equals kmin, which is T)
-  int32_t *out = a.idx + (size_t)h * a.l;
-  const uint32_t l = (uint32_t)a.l;
-  if constexpr (KEYS_IN_LDS) {
-    // 2. stable compaction, keys in LDS: thread t owns the run of `per` consecutive
-    // indices starting at t*per (per a multiple of 4, so each run is read with
-    // 16-byte loads into registers); one block-wide scan of the per-thread counts
-    // of keys > T and == T gives every thread its output positions.
-    constexpr int kMaxPer = kLdsKeys / kTopkThreads;   // 32
-    const int per = (((L + kTopkThreads - 1) / kTopkThreads) + 3) & ~3;
-    const int b = tid * per;
-    uint32_t kr[kMaxPer];
-    uint32_t ngt = 0, neq = 0;
+  // 2. per-chunk counts for the placement kernel: chunk c holds keys
+  // [c*kChunk, (c+1)*kChunk); the workspace gets, for every chunk, the number of
+  // keys > T and == T in the chunks before it.  A run of 16 consecutive keys is
+  // counted by one thread, so the 16 runs of a chunk are 16 adjacent lanes of one
+  // wave; groups of 1024 chunks are scanned in LDS (hist is free again) with a
+  // running carry.
+  static_assert(kChunk == 16 * kRun, "a chunk is 16 runs of adjacent lanes");
+  uint32_t *cnt = a.chunk_counts + (size_t)h * a.n_chunks * 2;
+  const int n_runs = (L + kRun - 1) / kRun;
+  uint32_t carry_gt = 0, carry_eq = 0;
+#pragma unroll 1
+  for (int c0 = 0; c0 < a.n_chunks; c0 += kTopkThreads) {
+    const int r_end = min(n_runs, (c0 + kTopkThreads) * 16);
+#pragma unroll 1
+    for (int rb = c0 * 16; rb < r_end; rb += kTopkThreads) {   // wave-uniform bounds
+      const int r = rb + tid;
+      uint32_t ngt = 0, neq = 0;
+      if (r < n_runs) {
+        uint32_t kr[kRun];
+        load_run<KEYS_IN_LDS>(a, srow, keys, r, kr);
 #pragma unroll
-    for (int j = 0; j < kMaxPer; j += 4) {
-      if (j < per) {
-        const uint4 q4 = *reinterpret_cast<const uint4 *>(&keys[b + j]);
-        kr[j] = q4.x;
-        kr[j + 1] = q4.y;
-        kr[j + 2] = q4.z;
-        kr[j + 3] = q4.w;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bool in = b + j + u < L;
-          ngt += (in && kr[j + u] > T) ? 1u : 0u;
-          neq += (in && kr[j + u] == T) ? 1u : 0u;
+        for (int u = 0; u < kRun; ++u) {
+          const bool in = r * kRun + u < L;
+          ngt += (in && kr[u] > T) ? 1u : 0u;
+          neq += (in && kr[u] == T) ? 1u : 0u;
         }
       }
+      uint32_t packed = (ngt << 16) | neq;            // each count <= 256
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) packed += (uint32_t)__shfl_xor((int)packed, m, 64);
+      if ((lane & 15) == 0 && r < n_runs) {
+        const int c = r / 16 - c0;
+        hist[c] = packed >> 16;
+        hist[kTopkThreads + c] = packed & 0xffffu;
+      }
     }
-    const uint32_t ig = wave_inclusive_scan(ngt, lane);
-    const uint32_t ie = wave_inclusive_scan(neq, lane);
+    __syncthreads();
+    const int c = c0 + tid;
+    const uint32_t vg = c < a.n_chunks ? hist[tid] : 0u;
+    const uint32_t ve = c < a.n_chunks ? hist[kTopkThreads + tid] : 0u;
+    const uint32_t ig = wave_inclusive_scan(vg, lane);
+    const uint32_t ie = wave_inclusive_scan(ve, lane);
     if (lane == 63) {
       wtot[0][wave] = ig;
       wtot[1][wave] = ie;
     }
     __syncthreads();
-    uint32_t g = ig - ngt, e = ie - neq;            // keys > T and == T before this run
-    for (int w = 0; w < wave; ++w) {
-      g += wtot[0][w];
-      e += wtot[1][w];
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      if (j < per && b + j < L) {
-        const uint32_t kk = kr[j];
-        if (kk > T) {
-          const uint32_t pos = g + min(e, need);
-          if (pos < l) out[pos] = b + j;
-          ++g;
-        } else if (kk == T) {
-          if (e < need && g + e < l) out[g + e] = b + j;
-          ++e;
-        }
+    uint32_t bg = 0, be = 0, tg = 0, te = 0;
+    for (int w = 0; w < kTopkWaves; ++w) {
+      const uint32_t xg = wtot[0][w], xe = wtot[1][w];
+      if (w < wave) {
+        bg += xg;
+        be += xe;
       }
+      tg += xg;
+      te += xe;
     }
-    return;
-  }
-  // 2. stable compaction: wave w owns indices [w*C, (w+1)*C), C a multiple of 64
-  const int C = ((L + kTopkThreads - 1) / kTopkThreads) * 64;
-  const int lo = min(wave * C, L);
-  const int hi = min(lo + C, L);
-  // f(i, key, valid) over this wave's run, 64 consecutive indices per step, in
-  // batches of kBatch steps
-  auto for_each_run_key = [&](auto &&f) {
-    for (int b0 = lo; b0 < hi; b0 += 64 * kBatch) {
-      uint32_t kb[kBatch];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) kb[j] = key_at(min(b0 + 64 * j + lane, hi - 1));
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int i = b0 + 64 * j + lane;
-        if (b0 + 64 * j < hi) f(i, kb[j], i < hi);   // wave-uniform step condition
-      }
+    if (c < a.n_chunks) {
+      cnt[2 * c] = carry_gt + bg + ig - vg;
+      cnt[2 * c + 1] = carry_eq + be + ie - ve;
     }
-  };
-  uint32_t ngt = 0, neq = 0;
-  for_each_run_key([&](int, uint32_t kk, bool valid) {
-    ngt += __popcll(__ballot(valid && kk > T));
-    neq += __popcll(__ballot(valid && kk == T));
-  });
-  if (lane == 0) {
-    wtot[0][wave] = ngt;
-    wtot[1][wave] = neq;
+    carry_gt += tg;
+    carry_eq += te;
+    __syncthreads();   // hist and wtot are rewritten by the next group
   }
-  __syncthreads();
-  uint32_t g_before = 0, e_before = 0;
-  for (int w = 0; w < wave; ++w) {
-    g_before += wtot[0][w];
-    e_before += wtot[1][w];
+  if (tid == 0) {
+    a.state[2 * h] = T;
+    a.state[2 * h + 1] = need;
   }
-  for_each_run_key([&](int i, uint32_t kk, bool valid) {
-    const bool gt = valid && kk > T;
-    const bool eq = valid && kk == T;
-    const unsigned long long bg = __ballot(gt);
-    const unsigned long long be = __ballot(eq);
-    const uint32_t g = g_before + lanes_below(bg);
-    const uint32_t e = e_before + lanes_below(be);
-    if (gt) {
-      const uint32_t pos = g + min(e, need);
-      if (pos < l) out[pos] = i;
-    } else if (eq && e < need) {
-      const uint32_t pos = g + e;
-      if (pos < l) out[pos] = i;
-    }
-    g_before += __popcll(bg);
-    e_before += __popcll(be);
-  });
 }
 
-// One workgroup per (slot s, tensor): copies row idx[h][s] of every kv head h.
-__global__ __launch_bounds__(128) void gather_kernel(const TopkArgs a) {
-  const int s = blockIdx.x;
-  const bool is_v = blockIdx.y != 0;
-  const int ch_log2 = (a.d == 128) ? 4 : 3;     // 16-byte chunks per head row: d / 8
-  const int n = a.Hkv << ch_log2;               // chunks in one [Hkv][d] row
-  const uint16_t *src_base = is_v ? a.v : a.k;
-  uint16_t *dst = (is_v ? a.vc : a.kc) + (size_t)s * n * 8;
-  for (int j = threadIdx.x; j < n; j += blockDim.x) {
-    const int hh = j >> ch_log2;
-    const int c = j & ((1 << ch_log2) - 1);
-    int tok = a.idx[(size_t)hh * a.l + s];
-    if ((unsigned)tok >= (unsigned)a.L) tok = 0;  // never read outside the block
-    const uint16_t *src = src_base + ((size_t)tok * a.Hkv + hh) * a.d + c * 8;
-    reinterpret_cast<uint4 *>(dst)[j] = *reinterpret_cast<const uint4 *>(src);
+// Compaction and gather, one workgroup per (chunk of kChunk keys, kv head).
+// Thread t takes key i = c*kChunk + t.  Keys > T are all kept; of the keys == T
+// the first `need` in index order are kept.  A kept key's output slot is the
+// number of kept keys before it: (keys > T before it) + min(keys == T before it,
+// need), from the chunk's counts plus wave ballots inside the chunk.  Kept keys
+// are listed in LDS, then the workgroup copies their K and V head rows with
+// 16-byte loads (consecutive threads on consecutive pieces of one row).
+__global__ __launch_bounds__(kChunk) void topk_place_gather_kernel(const TopkArgs a) {
+  __shared__ uint32_t wcnt[3][kChunk / 64];
+  __shared__ int32_t kept_tok[kChunk], kept_pos[kChunk];
+  const int c = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int L = a.L;
+  const uint32_t l = (uint32_t)a.l;
+  const int i = c * kChunk + tid;
+  const bool valid = i < L;
+  const uint32_t kk = valid ? order_key(a.scores[(size_t)h * L + i]) : 0u;
+  const uint32_t T = a.state[2 * h];
+  const uint32_t need = a.state[2 * h + 1];
+  const uint32_t *cnt = a.chunk_counts + ((size_t)h * a.n_chunks + c) * 2;
+  const bool gt = valid && kk > T;
+  const bool eq = valid && kk == T;
+  const unsigned long long bgt = __ballot(gt);
+  const unsigned long long beq = __ballot(eq);
+  if (lane == 0) {
+    wcnt[0][wave] = (uint32_t)__popcll(bgt);
+    wcnt[1][wave] = (uint32_t)__popcll(beq);
+  }
+  __syncthreads();
+  uint32_t g = cnt[0] + lanes_below(bgt), e = cnt[1] + lanes_below(beq);
+  for (int w = 0; w < wave; ++w) {
+    g += wcnt[0][w];
+    e += wcnt[1][w];
+  }
+  uint32_t pos = 0xffffffffu;
+  if (gt) pos = g + min(e, need);
+  else if (eq && e < need) pos = g + e;
+  const bool keep = pos < l;
+  const unsigned long long bk = __ballot(keep);
+  if (lane == 0) wcnt[2][wave] = (uint32_t)__popcll(bk);
+  __syncthreads();
+  uint32_t slot = lanes_below(bk);
+  uint32_t n_kept = 0;
+  for (int w = 0; w < kChunk / 64; ++w) {
+    if (w < wave) slot += wcnt[2][w];
+    n_kept += wcnt[2][w];
+  }
+  if (keep) {
+    a.idx[(size_t)h * l + pos] = i;
+    kept_tok[slot] = i;
+    kept_pos[slot] = (int32_t)pos;
+  }
+  __syncthreads();
+  // copy: piece p of tensor t of kept entry e, for j = (e * 2 + t) * CH + p
+  const int ch_log2 = (a.d == 128) ? 4 : 3;   // 16-byte pieces per head row: d / 8
+  const int n_pieces = (int)n_kept << (ch_log2 + 1);
+  const size_t row_stride = (size_t)a.Hkv * a.d;
+  for (int j = tid; j < n_pieces; j += kChunk) {
+    const int ent = j >> (ch_log2 + 1);
+    const bool is_v = (j >> ch_log2) & 1;
+    const int p = j & ((1 << ch_log2) - 1);
+    const size_t src = (size_t)kept_tok[ent] * row_stride + (size_t)h * a.d + p * 8;
+    const size_t dst = (size_t)kept_pos[ent] * row_stride + (size_t)h * a.d + p * 8;
+    const uint4 x = *reinterpret_cast<const uint4 *>((is_v ? a.v : a.k) + src);
+    *reinterpret_cast<uint4 *>((is_v ? a.vc : a.kc) + dst) = x;
   }
 }
 
 }  // namespace
 
-hipError_t launch_topk_gather(const TopkArgs &a, hipStream_t s) {
+size_t topk_workspace_bytes(int L, int Hkv) {
+  const size_t n_chunks = ((size_t)L + kChunk - 1) / kChunk;
+  const size_t bytes = (size_t)Hkv * 2 * sizeof(uint32_t) + (size_t)Hkv * n_chunks * 2 * sizeof(uint32_t);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+hipError_t launch_topk_gather(TopkArgs &a, void *workspace, hipStream_t s) {
+  a.n_chunks = (a.L + kChunk - 1) / kChunk;
+  a.state = static_cast<uint32_t *>(workspace);
+  a.chunk_counts = a.state + 2 * a.Hkv;
   if (a.L <= kLdsKeys) {
     hipLaunchKernelGGL((topk_select_kernel<true>), dim3(a.Hkv), dim3(kTopkThreads), 0, s, a);
   } else {
@@ -357,7 +431,7 @@ hipError_t launch_topk_gather(const TopkArgs &a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gather_kernel, dim3(a.l, 2), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(topk_place_gather_kernel, dim3(a.n_chunks, a.Hkv), dim3(kChunk), 0, s, a);
   return hipGetLastError();
 }
 

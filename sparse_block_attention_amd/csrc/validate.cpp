@@ -85,6 +85,7 @@ const char *apb_status_string(apb_status st) {
     case APB_OK: return "APB_OK";
     case APB_ERR_INVALID_ARGUMENT: return "APB_ERR_INVALID_ARGUMENT";
     case APB_ERR_UNSUPPORTED: return "APB_ERR_UNSUPPORTED";
+    case APB_ERR_WORKSPACE_TOO_SMALL: return "APB_ERR_WORKSPACE_TOO_SMALL";
     case APB_ERR_HIP: return "APB_ERR_HIP";
     case APB_ERR_INTERNAL: return "APB_ERR_INTERNAL";
   }

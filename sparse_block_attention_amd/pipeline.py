@@ -32,10 +32,10 @@ def problem_for(n_q_heads, n_kv_heads, head_dim, local_len, anchor_len, pass_per
                      host_index, n_hosts, kv_head_of_q)
 
 
-def compress(problem: B.Problem, scorer: dict, host: HostTensors, stream=None):
+def compress(problem: B.Problem, scorer: dict, host: HostTensors, stream=None, workspace=None):
     """(scores, idx, k_comp, v_comp) of one host's block."""
     scores = B.apb_score_kv(problem, scorer, host.q, host.k, host.v, stream=stream)
-    idx, kc, vc = B.apb_topk_gather(problem, scores, host.k, host.v, stream=stream)
+    idx, kc, vc = B.apb_topk_gather(problem, scores, host.k, host.v, workspace=workspace, stream=stream)
     return scores, idx, kc, vc
 
 
@@ -51,6 +51,7 @@ class StepBuffers:
     v_pass: Optional[torch.Tensor]
     out: torch.Tensor
     lse: torch.Tensor
+    topk_workspace: torch.Tensor
 
     @staticmethod
     def allocate(problem: B.Problem, device="cuda") -> "StepBuffers":
@@ -65,7 +66,8 @@ class StepBuffers:
             k_pass=torch.empty((P, Hkv, d), dtype=bf, device=device) if P else None,
             v_pass=torch.empty((P, Hkv, d), dtype=bf, device=device) if P else None,
             out=torch.empty((L, Hq, d), dtype=bf, device=device),
-            lse=torch.empty((Hq, L), dtype=f32, device=device))
+            lse=torch.empty((Hq, L), dtype=f32, device=device),
+            topk_workspace=B.topk_workspace(problem, device))
 
 
 def host_step(problem: B.Problem, scorer: dict, host: HostTensors, k_anchor, v_anchor,
@@ -86,7 +88,7 @@ def host_step(problem: B.Problem, scorer: dict, host: HostTensors, k_anchor, v_a
         side_stream.wait_stream(main)          # inputs of this step are ready
     B.apb_score_kv(problem, scorer, host.q, host.k, host.v, scores=buf.scores, stream=comp)
     B.apb_topk_gather(problem, buf.scores, host.k, host.v, idx=buf.idx, k_comp=buf.k_comp,
-                      v_comp=buf.v_comp, stream=comp)
+                      v_comp=buf.v_comp, workspace=buf.topk_workspace, stream=comp)
     if problem.pass_len:
         B.apb_build_passing(problem, k_comps, v_comps, k_pass=buf.k_pass, v_pass=buf.v_pass,
                             stream=main)

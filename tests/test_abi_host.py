@@ -56,10 +56,32 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert B.apb_abi_version() == 4
+    assert B.apb_abi_version() == 5
     assert B.apb_status_string(B.APB_OK) == "APB_OK"
     assert B.apb_status_string(B.APB_ERR_UNSUPPORTED) == "APB_ERR_UNSUPPORTED"
     assert B.apb_status_string(99) == "APB_ERR_UNKNOWN"
+
+
+def test_status_values_match_the_header(lib):
+    """The enum values are part of the ABI: read them from include/apb.h and compare with the
+    binding's constants and the library's names for them."""
+    text = open(HEADER).read()
+    body = text[text.index("typedef enum"):text.index("} apb_status;")]
+    values = {m.group(1): int(m.group(2)) for m in re.finditer(r"(APB_\w+)\s*=\s*(\d+)", body)}
+    assert values == {"APB_OK": 0, "APB_ERR_INVALID_ARGUMENT": 1, "APB_ERR_UNSUPPORTED": 2,
+                      "APB_ERR_WORKSPACE_TOO_SMALL": 3, "APB_ERR_HIP": 4, "APB_ERR_INTERNAL": 5}
+    for name, v in values.items():
+        assert getattr(B, name) == v
+        assert B.apb_status_string(v) == name
+
+
+def test_head_map_of_the_wrong_length_is_refused_before_the_call():
+    """The library reads n_q_heads entries of kv_head_of_q; a shorter list would be read past
+    its end and a longer one silently cut, so the binding refuses both."""
+    for bad in ([0, 1, 1], [0, 0, 1, 1, 0]):
+        with pytest.raises(ValueError, match="kv_head_of_q"):
+            _problem(kv_head_of_q=bad).to_c()
+    _problem(kv_head_of_q=[0, 1, 1, 0]).to_c()
 
 
 @pytest.mark.parametrize("kw,code,needle", [
@@ -179,6 +201,7 @@ def test_anchor_attention_and_rope_reject_bad_arguments(lib):
                               ({"heads": 5000}, B.APB_ERR_INVALID_ARGUMENT, "heads"),
                               ({"d": 96}, B.APB_ERR_UNSUPPORTED, "head_dim"),
                               ({"pos0": -1}, B.APB_ERR_INVALID_ARGUMENT, "pos0"),
+                              ({"pos0": (1 << 31) - 3}, B.APB_ERR_INVALID_ARGUMENT, "pos0"),
                               ({"base": 1.0}, B.APB_ERR_INVALID_ARGUMENT, "theta_base"),
                               ({"base": float("inf")}, B.APB_ERR_INVALID_ARGUMENT, "theta_base")]:
         a = dict(good, **bad)
@@ -204,7 +227,8 @@ def test_qkv_projection_rejects_bad_arguments(lib):
 def test_score_rejects_bad_scorer(lib):
     cp, keep = _problem().to_c()
     good = dict(hidden=64, w1=0x1000, b1=0x2000, w2=0x3000, b2=0x4000)
-    for bad, code in [({"hidden": 48}, B.APB_ERR_UNSUPPORTED), ({"hidden": 512}, B.APB_ERR_UNSUPPORTED),
+    for bad, code in [({"hidden": 40}, B.APB_ERR_UNSUPPORTED), ({"hidden": 272}, B.APB_ERR_UNSUPPORTED),
+                      ({"hidden": 8}, B.APB_ERR_UNSUPPORTED), ({"hidden": 512}, B.APB_ERR_UNSUPPORTED),
                       ({"w1": None}, B.APB_ERR_INVALID_ARGUMENT), ({"b2": 0x4008}, B.APB_ERR_INVALID_ARGUMENT)]:
         s = dict(good, **bad)
         sc = B._Scorer(s["hidden"], s["w1"], s["b1"], s["w2"], s["b2"])
@@ -217,10 +241,46 @@ def test_score_rejects_bad_scorer(lib):
                             None) == B.APB_ERR_INVALID_ARGUMENT
 
 
+def _ws_size(lib, pr):
+    cp, keep = pr.to_c()
+    return lib.apb_topk_workspace_size(ctypes.byref(cp))
+
+
+def test_topk_workspace_size(lib):
+    """8 bytes of selection state per kv head plus 8 bytes per 256-token chunk per kv head,
+    rounded up to 256 bytes; 0 for l == 0 and for an invalid problem."""
+    for L, Hkv in [(256, 2), (257, 2), (16384, 8), (131072, 8), (1, 1), (1 << 26, 8)]:
+        pr = _problem(local_len=L, n_kv_heads=Hkv, n_q_heads=2 * Hkv, pass_per_host=1, anchor_len=0)
+        chunks = -(-L // 256)
+        want = Hkv * 8 + Hkv * chunks * 8
+        want = -(-want // 256) * 256
+        assert _ws_size(lib, pr) == want, (L, Hkv)
+        assert B.apb_topk_workspace_size(pr) == want
+    assert _ws_size(lib, _problem(pass_per_host=0)) == 0
+    assert _ws_size(lib, _problem(head_dim=96)) == 0
+    assert "head_dim" in B.apb_last_error()
+
+
+def test_topk_rejects_a_small_or_missing_workspace(lib):
+    pr = _problem()
+    need = _ws_size(lib, pr)
+    cp, keep = pr.to_c()
+    ptrs = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000]
+    st = lib.apb_topk_gather(ctypes.byref(cp), *ptrs, 0x7000, need - 1, None)
+    assert st == B.APB_ERR_WORKSPACE_TOO_SMALL
+    assert str(need) in B.apb_last_error()
+    st = lib.apb_topk_gather(ctypes.byref(cp), *ptrs, None, 0, None)
+    assert st == B.APB_ERR_WORKSPACE_TOO_SMALL
+    st = lib.apb_topk_gather(ctypes.byref(cp), *ptrs, None, need, None)
+    assert st == B.APB_ERR_INVALID_ARGUMENT and "workspace" in B.apb_last_error()
+    st = lib.apb_topk_gather(ctypes.byref(cp), *ptrs, 0x7008, need, None)
+    assert st == B.APB_ERR_INVALID_ARGUMENT and "workspace" in B.apb_last_error()
+
+
 def test_topk_and_build_have_nothing_to_do_for_empty_sizes(lib):
-    # l == 0: nothing selected, nothing launched, NULL outputs allowed.
+    # l == 0: nothing selected, nothing launched, NULL outputs and workspace allowed.
     cp, keep = _problem(pass_per_host=0).to_c()
-    assert lib.apb_topk_gather(ctypes.byref(cp), None, None, None, None, None, None, None) == B.APB_OK
+    assert lib.apb_topk_gather(ctypes.byref(cp), None, None, None, None, None, None, None, 0, None) == B.APB_OK
     assert lib.apb_build_passing(ctypes.byref(cp), None, None, None, None, None) == B.APB_OK
     # host 0: no preceding hosts, empty passing block.
     cp, keep = _problem(host_index=0).to_c()
@@ -230,7 +290,7 @@ def test_topk_and_build_have_nothing_to_do_for_empty_sizes(lib):
 def test_topk_and_build_reject_bad_pointers(lib):
     cp, keep = _problem().to_c()
     assert lib.apb_topk_gather(ctypes.byref(cp), 0x1000, 0x2000, 0x3000, None, 0x5000, 0x6000,
-                               None) == B.APB_ERR_INVALID_ARGUMENT
+                               0x7000, 1 << 20, None) == B.APB_ERR_INVALID_ARGUMENT
     arr = (ctypes.c_void_p * 3)(0x1000, 0x2000, 0x3008)
     arr_ok = (ctypes.c_void_p * 3)(0x1000, 0x2000, 0x3000)
     assert lib.apb_build_passing(ctypes.byref(cp), arr_ok, arr, 0x4000, 0x5000, None) \

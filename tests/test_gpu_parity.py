@@ -111,6 +111,7 @@ def test_llama8b_full_size_sampled_rows():
     ("d64_multi_tile", 205, 5, 512, 128, 64, 8, 2, 64, 128, None),
     ("single_token", 206, 1, 1, 0, 1, 2, 1, 64, 32, None),
     ("l_equals_L", 207, 3, 96, 8, 96, 2, 1, 128, 32, None),
+    ("hidden_48", 209, 3, 277, 20, 40, 4, 2, 128, 48, None),
 ])
 def test_small_workloads_all_rows(cfg):
     name, cid, H, L, A, l, Hq, Hkv, d, Hs, hm = cfg

@@ -297,6 +297,32 @@ def test_rope_hand_values_and_position_zero():
     assert np.array_equal(orc.rope(y[:1], 0, 500000.0), y[:1])
 
 
+def test_rope_frequency_schedule_hand_values():
+    """The frequency of pair i is base^(-2i/d).  With base 10^4: d = 4 gives frequencies
+    1 and 10^-2, so at position 100 pair (0, 2) turns by 100 rad and pair (1, 3) by exactly
+    1 rad; d = 8 gives 1, 10^-1, 10^-2, 10^-3, so at position 1000 pairs 0..3 turn by
+    1000, 100, 10 and 1 rad.  The angles are written out by hand: another schedule (for
+    example base^(-i/d), which gives 10^-1 at d = 4) moves every pair but the first."""
+    for d, pos, angles in [(4, 100, [100.0, 1.0]), (8, 1000, [1000.0, 100.0, 10.0, 1.0])]:
+        half = d // 2
+        for i, a in enumerate(angles):
+            e_lo = np.zeros((1, 1, d))
+            e_lo[0, 0, i] = 1.0                      # first element of pair i
+            e_hi = np.zeros((1, 1, d))
+            e_hi[0, 0, i + half] = 1.0               # second element of pair i
+            want_lo = np.zeros(d)
+            want_lo[i], want_lo[i + half] = np.cos(a), np.sin(a)
+            want_hi = np.zeros(d)
+            want_hi[i], want_hi[i + half] = -np.sin(a), np.cos(a)
+            np.testing.assert_allclose(orc.rope(e_lo, pos, 10000.0)[0, 0], want_lo, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(orc.rope(e_hi, pos, 10000.0)[0, 0], want_hi, rtol=0, atol=1e-12)
+    # base 500000 (Llama 3) at d = 4: pair (1, 3) turns by sqrt(1 / 500000) rad per position
+    e = np.zeros((1, 1, 4))
+    e[0, 0, 1] = 1.0
+    a = 7.0 / np.sqrt(500000.0)
+    np.testing.assert_allclose(orc.rope(e, 7, 500000.0)[0, 0], [0, np.cos(a), 0, np.sin(a)], rtol=0, atol=1e-14)
+
+
 def test_rope_is_a_rotation_by_relative_position():
     """Pair norms are kept; <R(p) q, R(p') k> depends on p - p' only; R(a) then R(b) is R(a + b)."""
     q, k = _rand((1, 1, 64), 91), _rand((1, 1, 64), 92)
