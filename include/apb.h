@@ -143,6 +143,24 @@ apb_status apb_topk_gather(const apb_problem *problem, const float *scores,
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * apb_topk_gather for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same selection and gather, same outputs, with the workspace taken from a
+ * static array of APB_NOALLOC_TOPK_WORKSPACE_BYTES per GPU that the library
+ * holds until the process ends, instead of a caller buffer.  The call allocates
+ * nothing.  Problems whose workspace (apb_topk_workspace_size) exceeds that
+ * size return APB_ERR_UNSUPPORTED and launch nothing.  Every call on one GPU
+ * shares that GPU's array, so two calls whose kernels may overlap on one GPU
+ * (different streams, no ordering between them) race and give undefined
+ * results; calls ordered on one stream are safe.  Nothing in the array has to
+ * start at zero.
+ */
+#define APB_NOALLOC_TOPK_WORKSPACE_BYTES ((size_t)4 << 20)
+apb_status apb_topk_gather_noalloc(const apb_problem *problem, const float *scores,
+                                   const void *k_local, const void *v_local,
+                                   int32_t *idx, void *k_comp, void *v_comp, void *stream);
+
+/*
  * Step 3: passing block from the compressed blocks of hosts 0..p-1 (explainer,
  * "APB 的主要功能": the all-gathered compressed blocks form the passing block of
  * the preceding hosts' important KV; "APB 的技术原理": each block is compressed

@@ -26,6 +26,8 @@ APB_ERR_WORKSPACE_TOO_SMALL = 3
 APB_ERR_HIP = 4
 APB_ERR_INTERNAL = 5
 
+NOALLOC_TOPK_WORKSPACE_BYTES = 4 << 20   # APB_NOALLOC_TOPK_WORKSPACE_BYTES
+
 APB_SEG_ANCHOR = 1
 APB_SEG_PASSING = 2
 APB_SEG_LOCAL = 4
@@ -98,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.apb_score_kv.argtypes = [P, POINTER(_Scorer), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
         L.apb_topk_gather.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, ctypes.c_size_t, c_void_p]
+        L.apb_topk_gather_noalloc.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, c_void_p]
         L.apb_topk_workspace_size.argtypes = [P]
         L.apb_topk_workspace_size.restype = ctypes.c_size_t
         L.apb_build_passing.argtypes = [P, POINTER(c_void_p), POINTER(c_void_p), c_void_p, c_void_p,
@@ -121,8 +125,8 @@ def lib() -> ctypes.CDLL:
         L.apb_last_error.argtypes = []
         L.apb_last_error.restype = c_char_p
         L.apb_abi_version.argtypes = []
-        for name in ("apb_score_kv", "apb_topk_gather", "apb_build_passing", "apb_block_attention",
-                     "apb_block_attention_segments", "apb_merge_attention", "apb_anchor_attention",
+        for name in ("apb_score_kv", "apb_topk_gather", "apb_topk_gather_noalloc", "apb_build_passing",
+                     "apb_block_attention", "apb_block_attention_segments", "apb_merge_attention", "apb_anchor_attention",
                      "apb_rope", "apb_qkv_projection", "apb_validate_problem", "apb_abi_version"):
             getattr(L, name).restype = c_int
         _lib = L
@@ -225,6 +229,23 @@ def apb_topk_gather(problem: Problem, scores, k_local, v_local, idx=None, k_comp
                                workspace.data_ptr(), workspace.numel(), _stream(stream))
     del keep
     _check(st, "apb_topk_gather")
+    return idx, k_comp, v_comp
+
+
+def apb_topk_gather_noalloc(problem: Problem, scores, k_local, v_local, idx, k_comp, v_comp, stream=None):
+    """apb_topk_gather with the library's static per-GPU workspace (see include/apb.h).
+    The caller passes every output; nothing is allocated here or in the library."""
+    pr = problem
+    L, Hkv, d, l = pr.local_len, pr.n_kv_heads, pr.head_dim, pr.pass_per_host
+    cp, keep = pr.to_c()
+    st = lib().apb_topk_gather_noalloc(ctypes.byref(cp), _ptr(scores, "scores", torch.float32, (Hkv, L)),
+                                       _ptr(k_local, "k_local", torch.bfloat16, (L, Hkv, d)),
+                                       _ptr(v_local, "v_local", torch.bfloat16, (L, Hkv, d)),
+                                       _ptr(idx, "idx", torch.int32, (Hkv, l)),
+                                       _ptr(k_comp, "k_comp", torch.bfloat16, (l, Hkv, d)),
+                                       _ptr(v_comp, "v_comp", torch.bfloat16, (l, Hkv, d)), _stream(stream))
+    del keep
+    _check(st, "apb_topk_gather_noalloc")
     return idx, k_comp, v_comp
 
 

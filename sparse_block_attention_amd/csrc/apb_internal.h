@@ -117,6 +117,11 @@ struct TopkArgs {
 size_t topk_workspace_bytes(int L, int Hkv);
 hipError_t launch_topk_gather(TopkArgs &a, void *workspace, hipStream_t s);
 
+// Size of the per-GPU static workspace of apb_topk_gather_noalloc, and its device
+// address on the current device (looked up once per device).
+constexpr size_t kStaticTopkScratchBytes = APB_NOALLOC_TOPK_WORKSPACE_BYTES;
+hipError_t static_topk_scratch(void **ptr);
+
 // Passing-block assembly: up to 128 source blocks per launch.
 struct PassArgs {
   const uint16_t *ksrc[128];

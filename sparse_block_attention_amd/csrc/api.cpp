@@ -62,21 +62,20 @@ apb_status score_kv(const apb_problem *pr, const apb_scorer *sc, const void *q, 
   return hip_status(apb::launch_score_kv(a, static_cast<hipStream_t>(stream)), "apb_score_kv launch");
 }
 
-apb_status topk_gather(const apb_problem *pr, const float *scores, const void *k, const void *v, int32_t *idx,
-                       void *kc, void *vc, void *ws, size_t ws_bytes, void *stream) {
-  APB_TRY(apb_host::check_problem(pr));
-  if (pr->pass_per_host == 0) return APB_OK;
+// Checks shared by both top-l entry points (the problem is already valid, l > 0).
+apb_status check_topk_pointers(const float *scores, const void *k, const void *v, const int32_t *idx,
+                               const void *kc, const void *vc) {
   APB_TRY(need_ptr(scores, "scores"));
   APB_TRY(need_ptr(k, "k_local"));
   APB_TRY(need_ptr(v, "v_local"));
   APB_TRY(need_ptr(idx, "idx"));
   APB_TRY(need_ptr(kc, "k_comp"));
   APB_TRY(need_ptr(vc, "v_comp"));
-  const size_t need_bytes = apb::topk_workspace_bytes(pr->local_len, pr->n_kv_heads);
-  if (ws_bytes < need_bytes)
-    return fail(APB_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes = %zu, need %zu (apb_topk_workspace_size)", ws_bytes,
-                need_bytes);
-  APB_TRY(need_ptr(ws, "workspace"));
+  return APB_OK;
+}
+
+apb_status launch_topk(const apb_problem *pr, const float *scores, const void *k, const void *v, int32_t *idx,
+                       void *kc, void *vc, void *ws, void *stream) {
   apb::TopkArgs a;
   memset(&a, 0, sizeof a);
   a.scores = scores;
@@ -90,6 +89,35 @@ apb_status topk_gather(const apb_problem *pr, const float *scores, const void *k
   a.Hkv = pr->n_kv_heads;
   a.d = pr->head_dim;
   return hip_status(apb::launch_topk_gather(a, ws, static_cast<hipStream_t>(stream)), "apb_topk_gather launch");
+}
+
+apb_status topk_gather(const apb_problem *pr, const float *scores, const void *k, const void *v, int32_t *idx,
+                       void *kc, void *vc, void *ws, size_t ws_bytes, void *stream) {
+  APB_TRY(apb_host::check_problem(pr));
+  if (pr->pass_per_host == 0) return APB_OK;
+  APB_TRY(check_topk_pointers(scores, k, v, idx, kc, vc));
+  const size_t need_bytes = apb::topk_workspace_bytes(pr->local_len, pr->n_kv_heads);
+  if (ws_bytes < need_bytes)
+    return fail(APB_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes = %zu, need %zu (apb_topk_workspace_size)", ws_bytes,
+                need_bytes);
+  APB_TRY(need_ptr(ws, "workspace"));
+  return launch_topk(pr, scores, k, v, idx, kc, vc, ws, stream);
+}
+
+apb_status topk_gather_noalloc(const apb_problem *pr, const float *scores, const void *k, const void *v,
+                               int32_t *idx, void *kc, void *vc, void *stream) {
+  APB_TRY(apb_host::check_problem(pr));
+  if (pr->pass_per_host == 0) return APB_OK;
+  APB_TRY(check_topk_pointers(scores, k, v, idx, kc, vc));
+  const size_t need_bytes = apb::topk_workspace_bytes(pr->local_len, pr->n_kv_heads);
+  if (need_bytes > apb::kStaticTopkScratchBytes)
+    return fail(APB_ERR_UNSUPPORTED,
+                "apb_topk_gather_noalloc: this problem needs %zu bytes of workspace, the static workspace holds "
+                "%zu (APB_NOALLOC_TOPK_WORKSPACE_BYTES); use apb_topk_gather with a caller workspace",
+                need_bytes, apb::kStaticTopkScratchBytes);
+  void *ws = nullptr;
+  APB_TRY(hip_status(apb::static_topk_scratch(&ws), "apb_topk_gather_noalloc: static workspace address"));
+  return launch_topk(pr, scores, k, v, idx, kc, vc, ws, stream);
 }
 
 size_t topk_workspace_size(const apb_problem *pr) {
@@ -308,6 +336,11 @@ apb_status apb_topk_gather(const apb_problem *problem, const float *scores, cons
                            size_t workspace_bytes, void *stream) {
   APB_GUARD(topk_gather(problem, scores, k_local, v_local, idx, k_comp, v_comp, workspace, workspace_bytes,
                         stream));
+}
+
+apb_status apb_topk_gather_noalloc(const apb_problem *problem, const float *scores, const void *k_local,
+                                   const void *v_local, int32_t *idx, void *k_comp, void *v_comp, void *stream) {
+  APB_GUARD(topk_gather_noalloc(problem, scores, k_local, v_local, idx, k_comp, v_comp, stream));
 }
 
 apb_status apb_build_passing(const apb_problem *problem, const void *const *k_comp_hosts,

@@ -34,6 +34,8 @@
 // caller's workspace; every workspace word a call reads was written earlier in
 // that call.  The placement kernel spreads the compaction and the 16-byte row
 // copies over L/256 x Hkv workgroups.
+#include <mutex>
+
 #include "apb_internal.h"
 
 namespace apb {
@@ -413,6 +415,34 @@ __global__ __launch_bounds__(kChunk) void topk_place_gather_kernel(const TopkArg
 }
 
 }  // namespace
+
+// Workspace of the allocation-free entry point: one array per GPU, holding the
+// top-l workspace of the last call made on that GPU.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device address);
+// it uses the address hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) uint8_t scratch[kStaticTopkScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t static_topk_scratch(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t topk_workspace_bytes(int L, int Hkv) {
   const size_t n_chunks = ((size_t)L + kChunk - 1) / kChunk;

@@ -277,6 +277,24 @@ def test_topk_rejects_a_small_or_missing_workspace(lib):
     assert st == B.APB_ERR_INVALID_ARGUMENT and "workspace" in B.apb_last_error()
 
 
+def test_noalloc_topk_rejects_problems_beyond_its_static_workspace(lib):
+    """The allocation-free top-l refuses, before any launch, a problem whose workspace exceeds
+    the static array, and does nothing for l == 0."""
+    ptrs = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000]
+    big = _problem(local_len=1 << 26, n_kv_heads=8, n_q_heads=16, pass_per_host=1, anchor_len=0)
+    assert _ws_size(lib, big) > B.NOALLOC_TOPK_WORKSPACE_BYTES
+    cp, keep = big.to_c()
+    assert lib.apb_topk_gather_noalloc(ctypes.byref(cp), *ptrs, None) == B.APB_ERR_UNSUPPORTED
+    assert "static workspace" in B.apb_last_error()
+    cp, keep = _problem(pass_per_host=0).to_c()
+    assert lib.apb_topk_gather_noalloc(ctypes.byref(cp), None, None, None, None, None, None, None) == B.APB_OK
+    cp, keep = _problem().to_c()
+    assert lib.apb_topk_gather_noalloc(ctypes.byref(cp), None, *ptrs[1:], None) == B.APB_ERR_INVALID_ARGUMENT
+    text = open(HEADER).read()
+    assert "#define APB_NOALLOC_TOPK_WORKSPACE_BYTES ((size_t)4 << 20)" in text
+    assert B.NOALLOC_TOPK_WORKSPACE_BYTES == 4 << 20
+
+
 def test_topk_and_build_have_nothing_to_do_for_empty_sizes(lib):
     # l == 0: nothing selected, nothing launched, NULL outputs and workspace allowed.
     cp, keep = _problem(pass_per_host=0).to_c()
