@@ -30,7 +30,11 @@ Extra objects (skipped with --no-extras):
     the last host (every earlier token visible, no anchor);
   * `layer_sides`: the QKV projection of the host block, rotary embedding of
     its q and k, and the anchor's own causal attention (steps either side of
-    the attention step).
+    the attention step);
+  * `workloads`: the other layer shapes (tiny, Qwen-2.5-14B, Yi-34B-200K,
+    Llama-3-8B-1M), each step alone on seeded on-device inputs: attention
+    (mean, median, min, TFLOP/s, fraction of peak) and the a1, a2+a3 and a5
+    stages (warm and cold medians, fraction of HBM peak).
 """
 from __future__ import annotations
 
@@ -80,18 +84,22 @@ def attention_bytes(w) -> float:
 
 def stage_bytes(w) -> dict:
     """Algorithmic HBM bytes of the compression steps and the passing build of one host."""
-    L, Hq, Hkv, d, l, hs = (w.local_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.pass_per_host,
-                            w.hidden)
-    g = Hq // Hkv
+    L, Hq, Hkv, d, l = w.local_len, w.n_q_heads, w.n_kv_heads, w.head_dim, w.pass_per_host
     return {
-        # q, k, v of the block, W1, b1, w2 and b2 read; fp32 scores written
-        "a1_score": L * (Hq + 2 * Hkv) * d * 2 + Hkv * hs * (g + 2) * d * 2 + Hkv * (2 * hs + 1) * 4
-        + Hkv * L * 4,
+        # q, k, v of the block read; fp32 scores written (the scorer weights stay in L2
+        # and are not counted: scorer_weight_bytes)
+        "a1_score": L * (Hq + 2 * Hkv) * d * 2 + Hkv * L * 4,
         # scores read; l rows of K and V per kv head read and written; indices written
         "a2a3_topl_gather": Hkv * L * 4 + 2 * 2 * l * Hkv * d * 2 + Hkv * l * 4,
         # the earlier hosts' compressed blocks of K and V read and written once
         "a5_passing": 2 * 2 * w.pass_len * Hkv * d * 2,
     }
+
+
+def scorer_weight_bytes(w) -> int:
+    """W1 (bf16), b1, w2 and b2 (fp32) of all kv heads: read by the scorer, L2-resident."""
+    g = w.n_q_heads // w.n_kv_heads
+    return w.n_kv_heads * w.hidden * (g + 2) * w.head_dim * 2 + w.n_kv_heads * (2 * w.hidden + 1) * 4
 
 
 def _src_hash(path):
@@ -405,6 +413,97 @@ def cpu_baseline(w, blocks, weights, anchor, n_rows=4096):
     }
 
 
+def _attention_stats(ms_list, flops):
+    ms = np.asarray(ms_list, dtype=np.float64)
+    mean, med, mn = float(ms.mean()), float(np.median(ms)), float(ms.min())
+    return {"ms": mean, "ms_median": med, "ms_min": mn, "launches": int(ms.size),
+            "tflops": flops / (mean * 1e-3) / 1e12, "frac_bf16_peak": flops / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "tflop_per_launch": flops / 1e12}
+
+
+def other_workloads(B, names, reps=10, warm=3):
+    """Each step of the path alone at the other layer shapes, on seeded on-device inputs
+    (torch generator, N(0, 0.5^2) rounded to bf16; random compressed blocks of the earlier
+    hosts; random scorer weights): attention (HIP events around every launch, mean, median
+    and min) and the a1, a2+a3 and a5 stages (warm and cold medians).  Parity at these
+    shapes is covered by the GPU tests; this measures throughput."""
+    import torch
+    from sparse_block_attention_amd import pipeline, synth
+    res = {}
+    scratch = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    total = torch.zeros((), dtype=torch.int64, device="cuda")
+
+    def evict():
+        torch.sum(scratch.view(torch.int32), dim=0, out=total)
+
+    for name in names:
+        w = synth.WORKLOADS[name]
+        L, A, l, p = w.local_len, w.anchor_len, w.pass_per_host, w.host
+        Hq, Hkv, d, Hs = w.n_q_heads, w.n_kv_heads, w.head_dim, w.hidden
+        g = Hq // Hkv
+        print(f"# workload {name}", file=sys.stderr, flush=True)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(1000 + w.config_id)
+
+        def rnd(*shape, sigma=0.5):
+            return (torch.randn(shape, generator=gen, device="cuda") * sigma).to(torch.bfloat16)
+
+        pr = B.Problem(Hq, Hkv, d, L, A, l, p, w.n_hosts, None)
+        host = pipeline.HostTensors(rnd(L, Hq, d), rnd(L, Hkv, d), rnd(L, Hkv, d))
+        ka, va = (rnd(A, Hkv, d), rnd(A, Hkv, d)) if A else (None, None)
+        kcs = [rnd(l, Hkv, d) for _ in range(p)]
+        vcs = [rnd(l, Hkv, d) for _ in range(p)]
+        sc = {"w1": rnd(Hkv, Hs, (g + 2) * d, sigma=0.1),
+              "b1": torch.randn((Hkv, Hs), generator=gen, device="cuda") * 0.1,
+              "w2": torch.randn((Hkv, Hs), generator=gen, device="cuda") * 0.1,
+              "b2": torch.randn((Hkv,), generator=gen, device="cuda") * 0.1}
+        buf = pipeline.StepBuffers.allocate(pr)
+        byt = stage_bytes(w)
+        fns = {
+            "a1_score": lambda: B.apb_score_kv(pr, sc, host.q, host.k, host.v, scores=buf.scores),
+            "a2a3_topl_gather": lambda: B.apb_topk_gather(pr, buf.scores, host.k, host.v, idx=buf.idx,
+                                                          k_comp=buf.k_comp, v_comp=buf.v_comp,
+                                                          workspace=buf.topk_workspace),
+        }
+        if pr.pass_len:
+            fns["a5_passing"] = lambda: B.apb_build_passing(pr, kcs, vcs, k_pass=buf.k_pass, v_pass=buf.v_pass)
+        r = {"config": {"local_len": L, "anchor_len": A, "pass_len": pr.pass_len, "n_q_heads": Hq,
+                        "n_kv_heads": Hkv, "head_dim": d, "scorer_hidden": Hs}}
+        for st, fn in fns.items():
+            med, mn = _stage_times(fn, reps, warm)
+            cmed, _ = _stage_times(fn, reps, warm, evict=evict)
+            r[st] = {"us_median": med * 1e3, "us_min": mn * 1e3, "cold_us_median": cmed * 1e3, "bytes": byt[st],
+                     "frac_hbm_peak": byt[st] / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "cold_frac_hbm_peak": byt[st] / (cmed * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        for tag, key in (("warm", "us_median"), ("cold", "cold_us_median")):
+            t = r["a1_score"][key] + r["a2a3_topl_gather"][key]
+            b = byt["a1_score"] + byt["a2a3_topl_gather"]
+            r[tag + "_a1_a3"] = {"us_median": t, "frac_hbm_peak": b / (t * 1e-6) / 1e9 / PEAK_HBM_GBS}
+        attn = lambda: B.apb_block_attention(pr, host.q, ka, va, buf.k_pass, buf.v_pass, host.k, host.v,
+                                             out=buf.out, lse=buf.lse)
+        if pr.pass_len:
+            B.apb_build_passing(pr, kcs, vcs, k_pass=buf.k_pass, v_pass=buf.v_pass)
+        n_att = 3 if L > 65536 else reps
+        for _ in range(2):
+            attn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_att)]
+        for a, b in ev:
+            a.record()
+            attn()
+            b.record()
+        torch.cuda.synchronize()
+        r["attention"] = _attention_stats([a.elapsed_time(b) for a, b in ev], attention_flops(w))
+        t_step = (r["a1_score"]["us_median"] + r["a2a3_topl_gather"]["us_median"]
+                  + (r["a5_passing"]["us_median"] if pr.pass_len else 0.0)) * 1e-3 + r["attention"]["ms"]
+        r["prefill_tokens_per_s_serial_steps"] = L / (t_step * 1e-3)
+        res[name] = r
+        del host, ka, va, kcs, vcs, sc, buf
+        torch.cuda.empty_cache()
+    del scratch
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -493,7 +592,8 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    attn_times = [a.elapsed_time(b) for a, b in ev]
+    attn_ms = float(np.mean(attn_times))
     flops = attention_flops(w)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     traffic = measured_traffic(w.name)
@@ -515,8 +615,7 @@ def main():
                    "anchor_len": w.anchor_len, "pass_len": w.pass_len, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "scorer_hidden": w.hidden,
                    "host_index": w.host, "n_hosts": w.n_hosts},
-        "attention": {"ms": attn_ms, "tflops": achieved, "frac_bf16_peak": achieved / PEAK_BF16_TFLOPS,
-                      "tflop_per_launch": flops / 1e12},
+        "attention": _attention_stats(attn_times, flops),
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
     }
@@ -530,6 +629,12 @@ def main():
         result["modes"] = baseline_modes(B, w, host, prior_kv, attn_ms)
         result["layer_sides"] = layer_sides(B, w, host, ka, va)
     del buf, host, kcs, vcs, prior_kv
+    if not args.no_extras:
+        import torch as _t
+        _t.cuda.empty_cache()
+        others = [n for n in ("tiny", "qwen14b", "yi34b", "llama1m") if n != w.name]
+        result["workloads"] = other_workloads(B, others)
+        result["scorer_weight_bytes"] = scorer_weight_bytes(w)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle on a bounded sample)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, host_np, wts, (ka_np, va_np))

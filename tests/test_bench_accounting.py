@@ -74,9 +74,10 @@ def test_bench_refuses_more_than_one_gpu():
 
 
 def test_stage_bytes_are_the_arrays_each_step_moves(bench):
-    """Scorer: q, k, v of the block, the scorer weights and the fp32 scores; top-l +
-    gather: scores, K and V rows read and written, indices; passing: the earlier
-    hosts' compressed blocks read and written.  Sizes from the generator's arrays."""
+    """Scorer: q, k, v of the block and the fp32 scores (the scorer weights, L2-resident,
+    are reported apart); top-l + gather: scores, K and V rows read and written, indices;
+    passing: the earlier hosts' compressed blocks read and written.  Sizes from the
+    generator's arrays."""
     w = synth.Workload("acct_stage", 901, 3, 40, 8, 6, 4, 2, 64, 32, 1.0, 0)
     q, k, v = synth.host_block(w, w.host)
     wts = synth.scorer_weights(w)
@@ -85,7 +86,8 @@ def test_stage_bytes_are_the_arrays_each_step_moves(bench):
     bf16 = lambda a: a.size * 2
     kv_row = w.n_kv_heads * w.head_dim * 2
     b = bench.stage_bytes(w)
-    assert b["a1_score"] == (bf16(q) + bf16(k) + bf16(v) + bf16(wts["w1"]) + wts["b1"].size * 4
-                             + wts["w2"].size * 4 + wts["b2"].size * 4 + scores.nbytes)
+    assert b["a1_score"] == bf16(q) + bf16(k) + bf16(v) + scores.nbytes
+    assert bench.scorer_weight_bytes(w) == (bf16(wts["w1"]) + wts["b1"].size * 4 + wts["w2"].size * 4
+                                            + wts["b2"].size * 4)
     assert b["a2a3_topl_gather"] == scores.nbytes + 2 * 2 * w.pass_per_host * kv_row + idx.nbytes
     assert b["a5_passing"] == 2 * 2 * w.host * w.pass_per_host * kv_row
