@@ -67,6 +67,20 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
   return v;
 }
 
+// Sum of v over the 64 lanes of a wave, in every lane, with DPP moves: shifts by
+// 1, 2, 4 and 8 lanes inside each row of 16 (lanes whose source lies outside the
+// row add 0), lane 15 of each row added to the next row, lane 31 to the upper two
+// rows, then lane 63 read.
+__device__ __forceinline__ uint32_t wave_sum_dpp(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Batches of loads: every loop over the keys issues kBatch independent loads
 // before it uses any, so a thread waits for one memory latency per batch rather
 // than one per key.
@@ -134,8 +148,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const TopkArg
     if constexpr (KEYS_IN_LDS) return keys[i];
     else return order_key(srow[i]);
   };
-  // f(i, key) for i = tid, tid + 1024, ... < L, in batches of kBatch loads
+  // Rows whose fp32 scores start 16-byte aligned are read with 16-byte loads.
+  const bool vec = (L & 3) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
+  // f(i, key) for every key i < L, in batches of kBatch loads: from LDS (i = tid,
+  // tid + 1024, ...), or from the scores, 16-byte blocks when the row allows (block
+  // j of 4096 keys: thread t takes keys 4(j*1024 + t) .. +3).
   auto for_each_key = [&](bool from_scores, auto &&f) {
+    if (!KEYS_IN_LDS && vec) {
+      const int n4 = L >> 2;
+      const float4 *s4 = reinterpret_cast<const float4 *>(srow);
+      for (int base4 = 0; base4 < n4; base4 += kBatch * kTopkThreads) {
+        float4 fb[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) fb[j] = s4[min(base4 + j * kTopkThreads + tid, n4 - 1)];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int q = base4 + j * kTopkThreads + tid;
+          if (q < n4) {
+            f(4 * q, order_key(fb[j].x));
+            f(4 * q + 1, order_key(fb[j].y));
+            f(4 * q + 2, order_key(fb[j].z));
+            f(4 * q + 3, order_key(fb[j].w));
+          }
+        }
+      }
+      return;
+    }
     for (int base = 0; base < L; base += kBatch * kTopkThreads) {
       uint32_t kb[kBatch];
 #pragma unroll
@@ -278,15 +316,51 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(const TopkArg
   // counted by one thread, so the 16 runs of a chunk are 16 adjacent lanes of one
   // wave; groups of 1024 chunks are scanned in LDS (hist is free again) with a
   // running carry.
+  // Keys read from the scores with 16-byte loads are counted by blocks instead: a
+  // wave's share of a 4096-key block is one chunk, and a wave sum (DPP) counts it.
   static_assert(kChunk == 16 * kRun, "a chunk is 16 runs of adjacent lanes");
+  static_assert(kChunk * kTopkWaves == 4 * kTopkThreads, "a chunk is one wave's share of a key block");
   uint32_t *cnt = a.chunk_counts + (size_t)h * a.n_chunks * 2;
   const int n_runs = (L + kRun - 1) / kRun;
+  const bool by_blocks = !KEYS_IN_LDS && vec;
   uint32_t carry_gt = 0, carry_eq = 0;
 #pragma unroll 1
   for (int c0 = 0; c0 < a.n_chunks; c0 += kTopkThreads) {
-    const int r_end = min(n_runs, (c0 + kTopkThreads) * 16);
+    if (by_blocks) {
+      // chunks c0 .. c0+1023 are the wave shares of key blocks c0/16 .. c0/16+63
+      const int n4 = L >> 2;
+      const float4 *s4 = reinterpret_cast<const float4 *>(srow);
+      const int jb0 = c0 / kTopkWaves;
+      const int jb1 = min(jb0 + kTopkThreads / kTopkWaves, (n4 + kTopkThreads - 1) / kTopkThreads);
 #pragma unroll 1
-    for (int rb = c0 * 16; rb < r_end; rb += kTopkThreads) {   // wave-uniform bounds
+      for (int j0 = jb0; j0 < jb1; j0 += kBatch) {   // wave-uniform bounds
+        float4 fb[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) fb[j] = s4[min((j0 + j) * kTopkThreads + tid, n4 - 1)];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if (j0 + j < jb1) {   // wave-uniform
+            const int q = (j0 + j) * kTopkThreads + tid;
+            const uint32_t k4[4] = {order_key(fb[j].x), order_key(fb[j].y), order_key(fb[j].z), order_key(fb[j].w)};
+            uint32_t ngt = 0, neq = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const bool in = 4 * q + u < L;
+              ngt += (in && k4[u] > T) ? 1u : 0u;
+              neq += (in && k4[u] == T) ? 1u : 0u;
+            }
+            const uint32_t packed = wave_sum_dpp((ngt << 16) | neq);   // each count <= 256
+            const int c = (j0 + j) * kTopkWaves + wave - c0;
+            if (lane == 0 && c0 + c < a.n_chunks) {
+              hist[c] = packed >> 16;
+              hist[kTopkThreads + c] = packed & 0xffffu;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll 1
+    for (int rb = c0 * 16; !by_blocks && rb < min(n_runs, (c0 + kTopkThreads) * 16); rb += kTopkThreads) {
       const int r = rb + tid;
       uint32_t ngt = 0, neq = 0;
       if (r < n_runs) {
