@@ -103,8 +103,13 @@ def scorer_weight_bytes(w) -> int:
 
 
 def _src_hash(path):
+    """sha256 of a kernel source and the extra compiler options it is built with, so a
+    record taken on one build is not applied to another."""
+    from sparse_block_attention_amd import build as build_mod
     with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+        data = f.read()
+    flags = " ".join(build_mod.EXTRA_FLAGS.get(os.path.basename(path), []))
+    return hashlib.sha256(data + flags.encode()).hexdigest()
 
 
 def measured_traffic(workload: str):

@@ -29,6 +29,15 @@ HIP_FLAGS = [
 ]
 
 
+# Per-source compiler options.  The attention kernel is scheduled with LLVM's
+# max-ILP strategy: 0.3-0.5% faster than the default in three interleaved rounds of
+# 20 launches at the Llama-3.1-8B host shape (the iterative-ILP and max-memory-clause
+# strategies were 2.6% and 2.0% slower).
+EXTRA_FLAGS = {
+    "block_attention.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -42,7 +51,8 @@ def sources():
 
 def _compile(src: str, hipcc: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+    cmd = [hipcc, *HIP_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-I", INCLUDE, "-I", CSRC, "-c", src,
+           "-o", obj]
     if src.endswith(".cpp"):
         cmd = [hipcc, "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
