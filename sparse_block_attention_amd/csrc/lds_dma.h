@@ -1,7 +1,6 @@
 // LDS-DMA building blocks shared by the streaming MFMA kernels (scorer and
-// projection): chunks of 64-byte rows go HBM -> LDS with buffer_load ... lds,
-// 1 KB (16 rows) per instruction.  Device code for gfx950; included by .hip
-// sources only.
+// projection): chunk rows go HBM -> LDS with buffer_load ... lds, 1 KB per
+// instruction.  Device code for gfx950; included by .hip sources only.
 #pragma once
 
 #include "apb_internal.h"
@@ -10,10 +9,7 @@ namespace apb {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 16-byte piece p of chunk row r sits at piece p ^ swz(r).
-__device__ __forceinline__ int piece_swz(int r) { return (r >> 2) & 3; }
-
-// One 1 KB LDS-DMA load (16 rows x 64 bytes).  Base and range are the same in
+// One 1 KB LDS-DMA load (64 lanes x 16 bytes).  Base and range are the same in
 // every lane; readfirstlane says so, so the descriptor lives in scalar registers.
 // (Device pass only: the host pass has no buffer-descriptor type.)
 __device__ __forceinline__ void dma_1k(const void *base, int valid_bytes, int voff, uint8_t *dst) {
