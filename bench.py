@@ -629,10 +629,12 @@ def main():
         result["stages"] = stages(B, w, pr, sc, host, ka, va, kcs, vcs, buf)
         result["sclk_mhz_after"] = sclk_mhz()
     if not args.no_extras and prior_kv:
-        print("# split-phase attention and baseline modes", file=sys.stderr, flush=True)
+        print("# split-phase attention, steps either side, baseline modes", file=sys.stderr, flush=True)
         result["split_phase"] = split_phase(B, pr, host, ka, va, buf.k_pass, buf.v_pass, attn_ms)
-        result["modes"] = baseline_modes(B, w, host, prior_kv, attn_ms)
+        # The steps either side run before the baseline modes, whose 25 ms attention
+        # launches would otherwise leave them on a GPU clocked down by the heat.
         result["layer_sides"] = layer_sides(B, w, host, ka, va)
+        result["modes"] = baseline_modes(B, w, host, prior_kv, attn_ms)
     del buf, host, kcs, vcs, prior_kv
     if not args.no_extras:
         import torch as _t
