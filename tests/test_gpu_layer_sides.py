@@ -21,7 +21,8 @@ def _gpu():
 
 
 @pytest.mark.parametrize("A,Hq,Hkv,d,hm", [(1, 2, 1, 128, None), (300, 6, 3, 128, [2, 0, 1, 1, 0, 2]),
-                                            (2048, 32, 8, 128, None), (129, 4, 2, 64, None)])
+                                            (2048, 32, 8, 128, None), (129, 4, 2, 64, None),
+                                            (4095, 64, 8, 128, None)])  # 1024 items of 256 rows
 def test_anchor_attention(A, Hq, Hkv, d, hm):
     q = synth.random_bf16((A, Hq, d), 1, sigma=0.5, stream=A)
     k = synth.random_bf16((A, Hkv, d), 2, sigma=0.5, stream=A)

@@ -142,6 +142,30 @@ def test_attention_segment_edges(L, A, p, l, Hq, Hkv, d):
     check_attention(from_device_bf16(out), o_ref, _np(lse), lse_ref, "segment edges")
 
 
+@pytest.mark.parametrize("L,A,p,l,Hq,Hkv,d", [
+    (4001, 130, 3, 77, 64, 8, 128),   # 16 x 64 = 1024 row tiles of 256: the 256-row workgroups
+    (3841, 0, 2, 200, 96, 8, 128),    # no anchor; 15 x 96 = 1440 row tiles
+])
+def test_attention_256_row_workgroups_ragged(L, A, p, l, Hq, Hkv, d):
+    """Problems with at least 1024 work items of 256 query rows run the 8-wave
+    (256-row) workgroups the benchmark times; ragged segment ends and a ragged last
+    q tile, sampled rows of every head against the oracle."""
+    P = p * l
+    assert ((L + 255) // 256) * Hq >= 1024
+    q = synth.random_bf16((L, Hq, d), 11, stream=L)
+    ka, va = synth.random_bf16((A, Hkv, d), 12, stream=L), synth.random_bf16((A, Hkv, d), 13, stream=L)
+    kp, vp = synth.random_bf16((P, Hkv, d), 14, stream=L), synth.random_bf16((P, Hkv, d), 15, stream=L)
+    kl, vl = synth.random_bf16((L, Hkv, d), 16, stream=L), synth.random_bf16((L, Hkv, d), 17, stream=L)
+    pr = B.Problem(Hq, Hkv, d, L, A, l, p, p + 1, None)
+    dv = lambda x, n: to_device_bf16(x) if n else None
+    out, lse = B.apb_block_attention(pr, to_device_bf16(q), dv(ka, A), dv(va, A), dv(kp, P), dv(vp, P),
+                                     to_device_bf16(kl), to_device_bf16(vl))
+    torch.cuda.synchronize()
+    rows = sample_rows(L, 48, seed=L, tile=256)
+    o_ref, lse_ref = orc.block_attention(q, ka, va, kp, vp, kl, vl, rows=rows)
+    check_attention(from_device_bf16(out)[rows], o_ref, _np(lse)[:, rows], lse_ref, "256-row workgroups")
+
+
 @pytest.mark.parametrize("L,l,specials", [
     (1, 1, True), (7, 3, True), (256, 85, True), (16384, 1024, True), (16385, 5000, True),
     (16384, 16384, False), (131072, 4096, True), (3000, 2999, False),
