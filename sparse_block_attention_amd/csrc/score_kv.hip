@@ -289,6 +289,21 @@ void score_kv_kernel(const ScoreArgs a) {
   // ---- epilogue: lane holds hidden units mb*32 + 8*(i/4) + 4*half + i%4 of
   // tokens (th*4 + tb)*32 + lrow; partial w2 . relu(z + b1) per token, then
   // sum the four hidden quarters.
+  // b1 and w2 of this lane's hidden units (the same for all four token blocks),
+  // four consecutive units per 16-byte LDS read
+  float4 b1v[MBW][4], w2v[MBW][4];
+#pragma unroll
+  for (int j = 0; j < MBW; ++j) {
+    const int mb = hq + 4 * j;
+    if (mb < HB) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int u0 = mb * 32 + q4 * 8 + half * 4;
+        b1v[j][q4] = *reinterpret_cast<const float4 *>(sb1 + u0);
+        w2v[j][q4] = *reinterpret_cast<const float4 *>(sw2 + u0);
+      }
+    }
+  }
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     float part = 0.f;
@@ -298,8 +313,8 @@ void score_kv_kernel(const ScoreArgs a) {
       if (mb < HB) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int u = mb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          part = fmaf(sw2[u], fmaxf(acc[j][tb][i] + sb1[u], 0.f), part);
+          const float bb = b1v[j][i >> 2][i & 3], ww = w2v[j][i >> 2][i & 3];
+          part = fmaf(ww, fmaxf(acc[j][tb][i] + bb, 0.f), part);
         }
       }
     }
