@@ -95,8 +95,9 @@ __global__ __launch_bounds__(kThreads) void merge_attention_kernel(const MergeAr
           const size_t li = (size_t)head * a.L + row;
           la[u] = a.la[li];
           lb[u] = a.lb[li];
-          const u32x4 va = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.oa) + (size_t)row * per_row + c);
-          const u32x4 vb = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.ob) + (size_t)row * per_row + c);
+          const size_t ci = (size_t)row * per_row + c;
+          const u32x4 va = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.oa) + ci);
+          const u32x4 vb = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.ob) + ci);
           xa[u] = uint4{va[0], va[1], va[2], va[3]};
           xb[u] = uint4{vb[0], vb[1], vb[2], vb[3]};
         }
@@ -106,7 +107,8 @@ __global__ __launch_bounds__(kThreads) void merge_attention_kernel(const MergeAr
         const int row = r0 + u;
         if (row < row_end) {
           const MergeW mw = merge_weights(la[u], lb[u]);
-          reinterpret_cast<uint4 *>(a.out)[(size_t)row * per_row + c] = merge_chunk(xa[u], xb[u], mw.ca, mw.cb);
+          reinterpret_cast<uint4 *>(a.out)[(size_t)row * per_row + c] =
+              merge_chunk(xa[u], xb[u], mw.ca, mw.cb);
           if (a.lse != nullptr && lead) a.lse[(size_t)head * a.L + row] = mw.lse;
         }
       }

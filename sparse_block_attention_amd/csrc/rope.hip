@@ -10,10 +10,10 @@
 // a head row), forms their 8 angles once, and walks the row's heads, four at a
 // time with all loads issued first (non-temporal: each input byte is read once);
 // the d/16 threads of a row sit side by side, so each head row is read and
-// written as whole 128-byte pieces.  Against one workgroup per row with 8-byte
-// accesses, where the 16 threads sharing a pair range all computed its sin/cos:
-// q and k of a Llama-3.1-8B host block (336 MB) 86 -> 77 us, back to back.  The angle
-// pos * theta_i is formed and reduced modulo 2*pi in double precision
+// written as whole 128-byte pieces.  (Against one workgroup per row with 8-byte
+// accesses, where the 16 threads sharing a pair range all computed its sin and
+// cos: q and k of a Llama-3.1-8B host block, 336 MB, 86 -> 77 us back to back.)
+// The angle pos * theta_i is formed and reduced modulo 2*pi in double precision
 // (Cody-Waite with a two-part 2*pi): with positions below 2^31 the reduced angle
 // is within about 2^-21 rad of the exact one; sin/cos and the rotation run in
 // fp32 and each output is rounded once to bf16.
