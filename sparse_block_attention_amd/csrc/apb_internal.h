@@ -73,7 +73,7 @@ struct ProjArgs {
   const uint16_t *x;
   const uint16_t *w[3];
   uint16_t *c[3];
-  int N[3];                 // outputs of each matrix, N % 4 == 0
+  int N[3];                 // outputs of each matrix (heads x head_dim), N % 64 == 0
   int M, K;                 // K % 32 == 0
   int n_mt, n_nt;           // tiles of 256 along M; slices of 256 over all three N
   int slice_end[3];         // cumulative slice counts

@@ -25,8 +25,11 @@
 // read as zeros and ragged tiles need no special path; K % 64 == 32 adds one
 // half chunk.  Work items go in groups of 8 token tiles x all output slices,
 // token tile fastest, so the workgroups resident on one XCD at a time share a
-// few X tiles and a few W slices through that XCD's L2.  Each lane stores 4
-// consecutive outputs of one token (8 bytes) per accumulator group.
+// few X tiles and a few W slices through that XCD's L2.  The finished tile is
+// rounded to bf16 into the (by then idle) LDS ring and leaves in whole 512-byte
+// rows, 16 bytes per lane: stored straight from the accumulators, each store
+// instruction wrote 8 bytes into each of 32 rows, and that epilogue took about
+// an eighth of a workgroup's time.
 #include "lds_dma.h"
 
 namespace apb {
@@ -249,32 +252,47 @@ void proj_gemm_kernel(const ProjArgs a) {
     mfma_step(acc, g);
   }
 
-  // ---- epilogue: lane holds outputs n0 + ob*32 + 8*(i/4) + 4*half + i%4 of token
-  // m0 + (th*4 + tb)*32 + lrow; 4 consecutive outputs go out as one 8-byte store.
+  // ---- epilogue: the tile goes to LDS as bf16 (256 rows of 512 bytes, 16-byte
+  // pieces XOR-swizzled by row), then out in whole 512-byte rows.
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  barrier_lds_drained();    // every wave has read its last fragments from the ring
+  // Lane: token row (th*4 + tb)*32 + lrow, outputs ob*32 + 8*g4 + 4*half .. +3,
+  // i.e. half of 16-byte piece ob*4 + g4 of that row.
 #pragma unroll
   for (int j = 0; j < kOutB; ++j) {
     const int ob = oh * 4 + j;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const int m = (th * 4 + tb) * 32 + lrow;
-      if (m >= x_rows) continue;
-      uint16_t *crow = cmat + (size_t)(m0 + m) * N + n0;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int n = ob * 32 + g4 * 8 + half * 4;
-        if (n >= w_rows) continue;
+        const int piece = ob * 4 + g4;
         uint2 p;
         p.x = pack_bf16x2(acc[j][tb][g4 * 4 + 0], acc[j][tb][g4 * 4 + 1]);
         p.y = pack_bf16x2(acc[j][tb][g4 * 4 + 2], acc[j][tb][g4 * 4 + 3]);
-        *reinterpret_cast<uint2 *>(crow + n) = p;
+        *reinterpret_cast<uint2 *>(ring + m * 512 + ((piece ^ (m & 31)) << 4) + half * 8) = p;
       }
     }
+  }
+  barrier_lds_drained();
+  // Thread t writes piece t % 32 of row 8i + t / 32: two whole rows per wave.
+  const int piece = tid & 31;
+  const bool col_ok = piece * 8 < w_rows;   // w_rows is a multiple of 64
+#pragma unroll 4
+  for (int i = 0; i < kTile / (kThreads / 32); ++i) {
+    const int row = i * (kThreads / 32) + (tid >> 5);
+    if (row >= x_rows || !col_ok) continue;
+    const u32x4 val = *reinterpret_cast<const u32x4 *>(ring + row * 512 + ((piece ^ (row & 31)) << 4));
+    *reinterpret_cast<u32x4 *>(cmat + (size_t)(m0 + row) * N + n0 + piece * 8) = val;
   }
 }
 
 }  // namespace
 
 hipError_t launch_proj_gemm(ProjArgs &a, hipStream_t s) {
+  // the epilogue writes whole 16-byte pieces of output rows
+  for (int i = 0; i < 3; ++i)
+    if (a.N[i] < 64 || a.N[i] % 64 != 0) return hipErrorInvalidValue;
   a.n_mt = (a.M + kTile - 1) / kTile;
   int end = 0;
   for (int i = 0; i < 3; ++i) {
