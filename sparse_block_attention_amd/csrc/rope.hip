@@ -6,13 +6,15 @@
 // works the mlsanity.com APB page lists).
 //
 // gfx950 design: a pure HBM stream (read and write d*2 bytes per head row).  A
-// thread takes one token row and 8 consecutive pairs (16 bytes from each half of
-// a head row), forms their 8 angles once, and walks the row's heads, four at a
-// time with all loads issued first (non-temporal: each input byte is read once);
-// the d/16 threads of a row sit side by side, so each head row is read and
-// written as whole 128-byte pieces.  (Against one workgroup per row with 8-byte
-// accesses, where the 16 threads sharing a pair range all computed its sin and
-// cos: q and k of a Llama-3.1-8B host block, 336 MB, 86 -> 77 us back to back.)
+// thread takes one token row, 8 consecutive pairs (16 bytes from each half of a
+// head row) and every fourth head of the row: it forms its 8 angles once and walks
+// its heads four at a time, all loads issued first (non-temporal: each input byte
+// is read once).  The d/16 threads of a row and head sit side by side, so each
+// head row is read and written as whole 128-byte pieces.  Four threads share a
+// row's angles (each forms them) so that four times as many waves keep loads in
+// flight.  q and k of a Llama-3.1-8B host block, 336 MB, back to back: 86 us with
+// one workgroup per row and 8-byte accesses, 75 us with one thread per (row,
+// pairs) walking all heads, 68 us now.
 // The angle pos * theta_i is formed and reduced modulo 2*pi in double precision
 // (Cody-Waite with a two-part 2*pi): with positions below 2^31 the reduced angle
 // is within about 2^-21 rad of the exact one; sin/cos and the rotation run in
@@ -23,7 +25,9 @@ namespace apb {
 namespace {
 
 constexpr int kRopeThreads = 256;
-constexpr int kRopeUnroll = 4;  // heads whose loads are in flight together
+constexpr int kRopeSplitLog2 = 2;                 // threads per (row, pairs): 4
+constexpr int kRopeSplit = 1 << kRopeSplitLog2;   // each takes every fourth head
+constexpr int kRopeUnroll = 4;                    // heads whose loads are in flight together
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -57,9 +61,11 @@ __device__ __forceinline__ void rotate8(const uint4 lo, const uint4 hi, const fl
 
 __global__ __launch_bounds__(kRopeThreads) void rope_kernel(const RopeArgs a) {
   const int jpr_log2 = (a.d == 128) ? 3 : 2;          // 8-pair pieces per half row: d / 16
-  const int rows_per_wg = kRopeThreads >> jpr_log2;
+  const int tpr_log2 = jpr_log2 + kRopeSplitLog2;     // threads per row
+  const int rows_per_wg = kRopeThreads >> tpr_log2;
   const int j = threadIdx.x & ((1 << jpr_log2) - 1);  // this thread's pairs: 8j .. 8j+7
-  const int row = blockIdx.x * rows_per_wg + (threadIdx.x >> jpr_log2);
+  const int hs = (threadIdx.x >> jpr_log2) & (kRopeSplit - 1);  // heads hs, hs + 4, ...
+  const int row = blockIdx.x * rows_per_wg + (threadIdx.x >> tpr_log2);
   if (row >= a.rows) return;
   const int half_d = a.d >> 1;
   const double pos = (double)(a.pos0 + row);
@@ -76,24 +82,26 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(const RopeArgs a) {
   }
   const uint16_t *xr = a.x + (size_t)row * a.heads * a.d + 8 * j;
   uint16_t *orow = a.out + (size_t)row * a.heads * a.d + 8 * j;
-  for (int h0 = 0; h0 < a.heads; h0 += kRopeUnroll) {
+  for (int h0 = hs; h0 < a.heads; h0 += kRopeSplit * kRopeUnroll) {
     uint4 lo[kRopeUnroll], hi[kRopeUnroll];
 #pragma unroll
     for (int u = 0; u < kRopeUnroll; ++u) {
-      if (h0 + u < a.heads) {
-        const u32x4 vl = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr + (size_t)(h0 + u) * a.d));
-        const u32x4 vh = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr + (size_t)(h0 + u) * a.d + half_d));
+      const int h = h0 + kRopeSplit * u;
+      if (h < a.heads) {
+        const u32x4 vl = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr + (size_t)h * a.d));
+        const u32x4 vh = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr + (size_t)h * a.d + half_d));
         lo[u] = uint4{vl[0], vl[1], vl[2], vl[3]};
         hi[u] = uint4{vh[0], vh[1], vh[2], vh[3]};
       }
     }
 #pragma unroll
     for (int u = 0; u < kRopeUnroll; ++u) {
-      if (h0 + u < a.heads) {
+      const int h = h0 + kRopeSplit * u;
+      if (h < a.heads) {
         uint4 olo, ohi;
         rotate8(lo[u], hi[u], c, s, olo, ohi);
-        *reinterpret_cast<uint4 *>(orow + (size_t)(h0 + u) * a.d) = olo;
-        *reinterpret_cast<uint4 *>(orow + (size_t)(h0 + u) * a.d + half_d) = ohi;
+        *reinterpret_cast<uint4 *>(orow + (size_t)h * a.d) = olo;
+        *reinterpret_cast<uint4 *>(orow + (size_t)h * a.d + half_d) = ohi;
       }
     }
   }
@@ -102,7 +110,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(const RopeArgs a) {
 }  // namespace
 
 hipError_t launch_rope(const RopeArgs &a, hipStream_t s) {
-  const int rows_per_wg = kRopeThreads / (a.d / 16);
+  const int rows_per_wg = kRopeThreads / (a.d / 16) / kRopeSplit;
   hipLaunchKernelGGL(rope_kernel, dim3((a.rows + rows_per_wg - 1) / rows_per_wg), dim3(kRopeThreads), 0, s, a);
   return hipGetLastError();
 }
