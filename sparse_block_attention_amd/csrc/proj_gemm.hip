@@ -52,6 +52,9 @@ constexpr int kMfma = kOutB * 4;        // MFMAs per 16-wide K step
 constexpr int kReads = 4 + kOutB;       // LDS reads per K step
 constexpr int kKK = kKC / 16;           // K steps per chunk
 constexpr int kGroupM = 8;              // token tiles per work-item group
+constexpr int kOutRowB = kTile * 2;     // 512 bytes: one token's bf16 outputs in the staged tile
+static_assert(kTile * kOutRowB <= 2 * kSlot, "the staged output tile fits in the LDS ring");
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte piece p of chunk row r sits at piece p ^ swz(r): rows r .. r+15 of
 // one read cycle cover all 16 (row parity, piece) bank groups of 256 bytes.
@@ -254,7 +257,6 @@ void proj_gemm_kernel(const ProjArgs a) {
 
   // ---- epilogue: the tile goes to LDS as bf16 (256 rows of 512 bytes, 16-byte
   // pieces XOR-swizzled by row), then out in whole 512-byte rows.
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   barrier_lds_drained();    // every wave has read its last fragments from the ring
   // Lane: token row (th*4 + tb)*32 + lrow, outputs ob*32 + 8*g4 + 4*half .. +3,
   // i.e. half of 16-byte piece ob*4 + g4 of that row.
@@ -270,7 +272,7 @@ void proj_gemm_kernel(const ProjArgs a) {
         uint2 p;
         p.x = pack_bf16x2(acc[j][tb][g4 * 4 + 0], acc[j][tb][g4 * 4 + 1]);
         p.y = pack_bf16x2(acc[j][tb][g4 * 4 + 2], acc[j][tb][g4 * 4 + 3]);
-        *reinterpret_cast<uint2 *>(ring + m * 512 + ((piece ^ (m & 31)) << 4) + half * 8) = p;
+        *reinterpret_cast<uint2 *>(ring + m * kOutRowB + ((piece ^ (m & 31)) << 4) + half * 8) = p;
       }
     }
   }
@@ -282,7 +284,7 @@ void proj_gemm_kernel(const ProjArgs a) {
   for (int i = 0; i < kTile / (kThreads / 32); ++i) {
     const int row = i * (kThreads / 32) + (tid >> 5);
     if (row >= x_rows || !col_ok) continue;
-    const u32x4 val = *reinterpret_cast<const u32x4 *>(ring + row * 512 + ((piece ^ (row & 31)) << 4));
+    const u32x4 val = *reinterpret_cast<const u32x4 *>(ring + row * kOutRowB + ((piece ^ (row & 31)) << 4));
     *reinterpret_cast<u32x4 *>(cmat + (size_t)(m0 + row) * N + n0 + piece * 8) = val;
   }
 }
