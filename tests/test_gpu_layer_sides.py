@@ -38,7 +38,8 @@ def test_anchor_attention(A, Hq, Hkv, d, hm):
 
 @pytest.mark.parametrize("rows,heads,d,pos0,base", [
     (5, 3, 128, 0, 10000.0), (300, 8, 64, 123456, 500000.0), (17, 2, 128, (1 << 26) - 17, 500000.0),
-    (2048, 40, 128, 7 * 16384, 1000000.0), (17, 2, 128, (1 << 31) - 17, 500000.0)])
+    (2048, 40, 128, 7 * 16384, 1000000.0), (17, 2, 128, (1 << 31) - 17, 500000.0),
+    (7, 100, 64, 5, 10000.0), (9, 1, 128, 3, 10000.0)])
 def test_rope_matches_oracle(rows, heads, d, pos0, base):
     """Bar: the kernel rounds an fp32 rotation once to bf16 (half an ulp, 2^-9 relative) after
     fp32 sin/cos of an angle reduced in double: |o - o_ref| <= 2^-8 |o_ref| + 1e-5."""
